@@ -1,0 +1,469 @@
+/*
+ * pact_oracle.c -- plain, slow CPU oracle (TEST INFRASTRUCTURE ONLY; see the
+ * header).  Every function is written for obviousness, not speed: roundings to
+ * a small value set are done by scanning that set, sums run in index order.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math).
+ */
+#include "pact_oracle.h"
+
+#include <assert.h>
+#include <math.h>
+#include <quadmath.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------- */
+/* BF16 <-> FP32                                                              */
+/* ------------------------------------------------------------------------- */
+float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round-to-nearest-even onto the BF16 grid: keep the top 16 bits, and round
+ * up when the dropped 16 bits exceed half, or equal half with an odd kept LSB.
+ * Finite inputs only (the data flow never produces Inf/NaN). */
+uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* ------------------------------------------------------------------------- */
+/* E2M1 and E4M3 ([blog] FAQ: 16 E2M1 elements share one E4M3 block scale)    */
+/* ------------------------------------------------------------------------- */
+/* E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa; exponent 0 is
+ * subnormal (0 or 0.5).  No Inf/NaN. */
+float orc_e2m1_value(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    float mag = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3 (OCP "FN" variant): bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0
+ * mantissa; exponent 0 is subnormal; 0x7F/0xFF are NaN; no Inf; max 448. */
+float orc_e4m3_value(uint8_t b) {
+    int s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    float mag = (e == 0) ? ldexpf((float)m / 8.0f, -6) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest element of an ascending value table, ties to the even index (for
+ * both formats the index LSB is the mantissa LSB, so this is IEEE
+ * round-to-nearest-even onto the format); values past the top saturate. */
+static int nearest_even_index(double t, const double *vals, int n) {
+    if (t >= vals[n - 1]) return n - 1;
+    int lo = 0;
+    for (int i = 0; i < n; ++i)
+        if (vals[i] <= t) lo = i;
+    if (vals[lo] == t) return lo;
+    int hi = lo + 1;
+    double dlo = t - vals[lo], dhi = vals[hi] - t; /* exact: operands are close */
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo % 2 == 0) ? lo : hi;
+}
+
+uint8_t orc_e2m1_encode_mag(float r) {
+    static const double mags[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    assert(r >= 0.0f);
+    return (uint8_t)nearest_even_index((double)r, mags, 8);
+}
+
+static double g_e4m3_vals[127]; /* the 127 finite non-negative E4M3 values, ascending */
+
+__attribute__((constructor)) static void init_e4m3_vals(void) {
+    for (int b = 0; b < 127; ++b) g_e4m3_vals[b] = (double)orc_e4m3_value((uint8_t)b);
+}
+
+uint8_t orc_e4m3_encode(float t) {
+    assert(t >= 0.0f);
+    return (uint8_t)nearest_even_index((double)t, g_e4m3_vals, 127);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Row quantizer Q                                                            */
+/* Reading of the pages (silent on everything past "16 E2M1 + one E4M3"):     */
+/*  - a second-level FP32 scale per row, d = amax_row / (6*448), so the row's */
+/*    largest block takes the largest E4M3 scale;                              */
+/*  - block scale = E4M3 round-to-nearest-even of amax_block / (6 d), clamped */
+/*    to 448;                                                                  */
+/*  - element code = E2M1 round-to-nearest-even of |x| / (scale * d), clamped */
+/*    to 6, sign kept (also for zero), by a true IEEE binary32 division.       */
+/* ------------------------------------------------------------------------- */
+static void quantize_row(const float *x, int64_t cols, uint8_t *codes, uint8_t *scales,
+                         float *d_out) {
+    if (cols <= 0) {
+        *d_out = 0.0f;
+        return;
+    }
+    float amax = 0.0f;
+    for (int64_t j = 0; j < cols; ++j) {
+        assert(isfinite(x[j]));
+        float a = fabsf(x[j]);
+        if (a > amax) amax = a;
+    }
+    float d = amax / 2688.0f; /* 2688 = 6 * 448 */
+    *d_out = d;
+    memset(codes, 0, (size_t)(cols / 2));
+    if (d == 0.0f) {
+        for (int64_t b = 0; b < cols / 16; ++b) scales[b] = 0;
+        for (int64_t j = 0; j < cols; ++j) {
+            uint8_t code = (uint8_t)(signbit(x[j]) ? 8 : 0);
+            codes[j / 2] |= (uint8_t)((j % 2) ? (code << 4) : code);
+        }
+        return;
+    }
+    float D = 6.0f * d;
+    for (int64_t b = 0; b < cols / 16; ++b) {
+        float ab = 0.0f;
+        for (int64_t j = 16 * b; j < 16 * b + 16; ++j) {
+            float a = fabsf(x[j]);
+            if (a > ab) ab = a;
+        }
+        float t = ab / D;
+        uint8_t sb = orc_e4m3_encode(t);
+        scales[b] = sb;
+        float S = orc_e4m3_value(sb) * d;
+        for (int64_t j = 16 * b; j < 16 * b + 16; ++j) {
+            uint8_t mag = 0;
+            if (S != 0.0f) mag = orc_e2m1_encode_mag(fabsf(x[j]) / S);
+            uint8_t code = (uint8_t)((signbit(x[j]) ? 8 : 0) | mag);
+            codes[j / 2] |= (uint8_t)((j % 2) ? (code << 4) : code);
+        }
+    }
+}
+
+void orc_quantize_rows_f32(const float *x, int64_t ld, int64_t rows, int64_t cols,
+                           uint8_t *codes, uint8_t *scales, float *d) {
+    assert(cols % 16 == 0);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        quantize_row(x + i * ld, cols, codes + i * (cols / 2), scales + i * (cols / 16), d + i);
+}
+
+void orc_quantize_rows_bf16(const uint16_t *x, int64_t ld, int64_t rows, int64_t cols,
+                            uint8_t *codes, uint8_t *scales, float *d) {
+    assert(cols % 16 == 0);
+#pragma omp parallel
+    {
+        float *row = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            for (int64_t j = 0; j < cols; ++j) row[j] = orc_bf16_to_f32(x[i * ld + j]);
+            quantize_row(row, cols, codes + i * (cols / 2), scales + i * (cols / 16), d + i);
+        }
+        free(row);
+    }
+}
+
+static float operand_value(const uint8_t *codes, const uint8_t *scales, int64_t j) {
+    uint8_t byte = codes[j / 2];
+    uint8_t code = (uint8_t)((j % 2) ? (byte >> 4) : (byte & 15));
+    return orc_e2m1_value(code) * orc_e4m3_value(scales[j / 16]); /* exact */
+}
+
+void orc_operand_values(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                        int64_t cols, float *b) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            b[i * cols + j] = operand_value(codes + i * (cols / 2), scales + i * (cols / 16), j);
+}
+
+void orc_dequantize(const uint8_t *codes, const uint8_t *scales, const float *d,
+                    int64_t rows, int64_t cols, float *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            out[i * cols + j] =
+                operand_value(codes + i * (cols / 2), scales + i * (cols / 16), j) * d[i];
+}
+
+/* ------------------------------------------------------------------------- */
+/* RMSNorm ([blog] Method bullet 2: the quantized RMSNorm output is what the  */
+/* backward reuses; bullet 4: quantization is fused into the norm kernel).    */
+/* Reading: the quantizer sees the BF16-rounded norm output, exactly what a   */
+/* separate quantize kernel would read.                                       */
+/* ------------------------------------------------------------------------- */
+
+/* Exact sum of squares: every BF16 value is M * 2^k with integer M < 256 and
+ * -133 <= k <= 120, so x^2 = M^2 * 2^(2k) is an integer multiple of 2^-266.
+ * Sum those integers in a 640-bit accumulator, then round once to binary64. */
+#define SQ_LIMBS 10
+double orc_sumsq_bf16(const uint16_t *x, int64_t n) {
+    uint64_t acc[SQ_LIMBS];
+    memset(acc, 0, sizeof acc);
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t e = (x[i] >> 7) & 0xFF, f = x[i] & 0x7F;
+        assert(e != 0xFF);
+        uint64_t M = (e == 0) ? f : (128u + f);
+        int k = (e == 0) ? -133 : (int)e - 127 - 7;
+        if (M == 0) continue;
+        uint64_t sq = M * M;                  /* < 2^16 */
+        int pos = 2 * k + 266;                /* bit position of the unit */
+        int limb = pos / 64, sh = pos % 64;
+        unsigned __int128 v = (unsigned __int128)sq << sh;
+        uint64_t carry = 0;
+        for (int L = limb; L < SQ_LIMBS; ++L) {
+            unsigned __int128 add = (L == limb) ? (uint64_t)v : (L == limb + 1) ? (uint64_t)(v >> 64) : 0;
+            unsigned __int128 s = (unsigned __int128)acc[L] + add + carry;
+            acc[L] = (uint64_t)s;
+            carry = (uint64_t)(s >> 64);
+            if (L > limb + 1 && carry == 0) break;
+        }
+        assert(carry == 0);
+    }
+    /* locate the top set bit */
+    int top = -1;
+    for (int L = SQ_LIMBS - 1; L >= 0 && top < 0; --L)
+        if (acc[L]) top = L * 64 + 63 - __builtin_clzll(acc[L]);
+    if (top < 0) return 0.0;
+#define BIT(p) ((p) < 0 ? 0u : (unsigned)((acc[(p) / 64] >> ((p) % 64)) & 1u))
+    /* take 53 bits [top-52, top], then round to nearest even using the rest */
+    uint64_t mant = 0;
+    for (int p = top; p > top - 53; --p) mant = (mant << 1) | BIT(p);
+    int lsb = top - 52;
+    unsigned round_bit = BIT(lsb - 1);
+    unsigned sticky = 0;
+    for (int p = lsb - 2; p >= 0; --p) sticky |= BIT(p);
+#undef BIT
+    if (round_bit && (sticky || (mant & 1u))) mant += 1; /* may carry to 2^53: still exact */
+    return ldexp((double)mant, lsb - 266);
+}
+
+void orc_rmsnorm_quant(const uint16_t *x, int64_t ld, const uint16_t *gamma, float eps,
+                       int64_t rows, int64_t cols, uint16_t *y, uint8_t *codes,
+                       uint8_t *scales, float *d, float *rstd) {
+    assert(cols % 16 == 0);
+#pragma omp parallel
+    {
+        float *row = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const uint16_t *xi = x + i * ld;
+            double ss = orc_sumsq_bf16(xi, cols);
+            double ms = ss / (double)cols;
+            double v = ms + (double)eps;
+            double rt = sqrt(v);
+            double inv = 1.0 / rt;
+            float r = (float)inv;
+            if (rstd) rstd[i] = r;
+            for (int64_t j = 0; j < cols; ++j) {
+                float t = orc_bf16_to_f32(xi[j]) * r;
+                float t2 = t * orc_bf16_to_f32(gamma[j]);
+                uint16_t yb = orc_f32_to_bf16(t2);
+                if (y) y[i * cols + j] = yb;
+                row[j] = orc_bf16_to_f32(yb);
+            }
+            quantize_row(row, cols, codes + i * (cols / 2), scales + i * (cols / 16), d + i);
+        }
+        free(row);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* SiLU * mul ([blog] Method bullet 2: forward keeps BF16 inputs, an NVFP4   */
+/* copy of gate/up is kept for backward; [abstract]).                         */
+/* Reading: sigma32(g) is the correctly rounded binary32 value of            */
+/* g / (1 + exp(-g)); h = bf16(sigma32(g) * u) with one binary32 multiply.    */
+/* ------------------------------------------------------------------------- */
+static float g_sig_table[65536];
+static int g_sig_unsafe = -1; /* -1: not built; else count of undecided inputs */
+
+/* Quad-precision (binary128, 113-bit significand) evaluation, then one
+ * rounding to binary32.  The evaluation error is a few units of 2^-113
+ * relative.  Small |g| puts the value within about g^3/24 (relative) of a
+ * binary32 rounding midpoint (g/2 + g^2/4 can be a midpoint exactly), which is
+ * still far above 2^-100 for every BF16 input that does not round to g/2; an
+ * input is flagged if its quad value lies within 2^-100 of a midpoint. */
+static float sigmoid_q(uint16_t gb, int *unsafe) {
+    __float128 g = (__float128)orc_bf16_to_f32(gb);
+    __float128 e = expq(-g);
+    __float128 v = g / (1.0Q + e);
+    float r = (float)v;
+    *unsafe = 0;
+    if (v != 0.0Q && (__float128)r != v) {
+        float nb = ((__float128)r < v) ? nextafterf(r, INFINITY) : nextafterf(r, -INFINITY);
+        __float128 mid = ((__float128)r + (__float128)nb) / 2.0Q; /* exact */
+        __float128 dist = fabsq(v - mid), mag = fabsq(v);
+        if (dist <= mag * ldexpq(1.0Q, -100)) *unsafe = 1;
+    }
+    return r;
+}
+
+static void build_sig_table(void) {
+    int bad = 0;
+    for (uint32_t b = 0; b < 65536; ++b) {
+        uint32_t e = (b >> 7) & 0xFF;
+        if (e == 0xFF) { g_sig_table[b] = NAN; continue; }
+        int u;
+        g_sig_table[b] = sigmoid_q((uint16_t)b, &u);
+        bad += u;
+    }
+    g_sig_unsafe = bad;
+}
+
+int orc_sigmoid_check_table(void) {
+    if (g_sig_unsafe < 0) build_sig_table();
+    return g_sig_unsafe;
+}
+
+float orc_sigmoid_mul_g(uint16_t g_bits) {
+    if (g_sig_unsafe < 0) build_sig_table();
+    return g_sig_table[g_bits];
+}
+
+void orc_silu_mul_quant(const uint16_t *g, const uint16_t *u, int64_t ld, int64_t rows,
+                        int64_t cols, uint16_t *h,
+                        uint8_t *hc, uint8_t *hs, float *hd,
+                        uint8_t *gc, uint8_t *gs, float *gd,
+                        uint8_t *uc, uint8_t *us, float *ud) {
+    assert(cols % 16 == 0);
+    if (g_sig_unsafe < 0) build_sig_table();
+    assert(g_sig_unsafe == 0);
+#pragma omp parallel
+    {
+        float *hrow = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            for (int64_t j = 0; j < cols; ++j) {
+                float sg = g_sig_table[g[i * ld + j]];
+                float p = sg * orc_bf16_to_f32(u[i * ld + j]);
+                uint16_t hb = orc_f32_to_bf16(p);
+                if (h) h[i * cols + j] = hb;
+                hrow[j] = orc_bf16_to_f32(hb);
+            }
+            quantize_row(hrow, cols, hc + i * (cols / 2), hs + i * (cols / 16), hd + i);
+        }
+        free(hrow);
+    }
+    if (gc) orc_quantize_rows_bf16(g, ld, rows, cols, gc, gs, gd);
+    if (uc) orc_quantize_rows_bf16(u, ld, rows, cols, uc, us, ud);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Weight layouts ([blog] Method bullet 4: forward and backward NVFP4 weight  */
+/* layouts are rebuilt, transposed and re-quantized once, then cached).       */
+/* Reading: the backward layout is built from the forward NVFP4 weights       */
+/* reconstructed in FP32 (R = b * d, one rounding), transposed, and quantized */
+/* by Q along the rows of R^T (blocks of 16 along N).                          */
+/* ------------------------------------------------------------------------- */
+void orc_build_weight_layouts(const uint16_t *W, int64_t N, int64_t K,
+                              uint8_t *fc, uint8_t *fs, float *fd,
+                              uint8_t *bc, uint8_t *bs, float *bd, int use_given_fwd) {
+    assert(K % 16 == 0 && N % 16 == 0);
+    if (!use_given_fwd) orc_quantize_rows_bf16(W, K, N, K, fc, fs, fd);
+    float *Rt = (float *)malloc(sizeof(float) * (size_t)(N * K > 0 ? N * K : 1));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            Rt[k * N + n] = operand_value(fc + n * (K / 2), fs + n * (K / 16), k) * fd[n];
+    orc_quantize_rows_f32(Rt, N, K, N, bc, bs, bd);
+    free(Rt);
+}
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4 GEMM + BF16 LoRA term                                                */
+/* [blog] Method bullet 1: frozen projections run as NVFP4 GEMMs with FP32    */
+/* accumulation and BF16 output, forward and input-gradient; final note of   */
+/* the Method section: adapters A, B stay BF16.  [peft] LoRA: h = W0 x + BAx. */
+/* Readings: the adapters multiply the BF16 activation (not its NVFP4 copy);  */
+/* the rank-r intermediate is rounded to BF16; the LoRA term is scaled by s   */
+/* and added after the frozen output is scaled by both row scales; an        */
+/* optional BF16 C (residual) is added last; one BF16 rounding at the end.    */
+/* ------------------------------------------------------------------------- */
+static void gemm_tn_rows(const uint8_t *ac, const uint8_t *as, const float *ad, int64_t Kc,
+                         const uint8_t *bcodes, const uint8_t *bscales, const float *bdv,
+                         int64_t Nout,
+                         const uint16_t *Xl, int64_t Kl, /* LoRA input rows, length Kl */
+                         const uint16_t *P, int64_t p_sj, int64_t p_sk, /* P[j,k2] strides */
+                         const uint16_t *Q, int64_t q_sn, int64_t q_sj, /* Q[n,j] strides */
+                         int32_t r, float s, const uint16_t *C,
+                         const int64_t *row_idx, int64_t n_rows, uint16_t *out) {
+    float *bvals = (float *)malloc(sizeof(float) * (size_t)(Nout * Kc > 0 ? Nout * Kc : 1));
+    orc_operand_values(bcodes, bscales, Nout, Kc, bvals);
+#pragma omp parallel
+    {
+        float *avals = (float *)malloc(sizeof(float) * (size_t)(Kc > 0 ? Kc : 1));
+        float T[1024];
+        assert(r <= 1024);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            int64_t m = row_idx[i];
+            for (int64_t k = 0; k < Kc; ++k)
+                avals[k] = operand_value(ac + m * (Kc / 2), as + m * (Kc / 16), k);
+            for (int32_t j = 0; j < r; ++j) {
+                float t = 0.0f;
+                for (int64_t k2 = 0; k2 < Kl; ++k2) {
+                    float p = orc_bf16_to_f32(Xl[m * Kl + k2]) * orc_bf16_to_f32(P[j * p_sj + k2 * p_sk]);
+                    t = t + p;
+                }
+                T[j] = orc_bf16_to_f32(orc_f32_to_bf16(t));
+            }
+            for (int64_t n = 0; n < Nout; ++n) {
+                const float *bn = bvals + n * Kc;
+                float acc = 0.0f;
+                for (int64_t k = 0; k < Kc; ++k) {
+                    float p = avals[k] * bn[k];
+                    acc = acc + p;
+                }
+                float y = acc * ad[m];
+                y = y * bdv[n];
+                if (r > 0) {
+                    float L = 0.0f;
+                    for (int32_t j = 0; j < r; ++j) {
+                        float p = T[j] * orc_bf16_to_f32(Q[n * q_sn + j * q_sj]);
+                        L = L + p;
+                    }
+                    float sl = s * L;
+                    y = y + sl;
+                }
+                if (C) y = y + orc_bf16_to_f32(C[m * Nout + n]);
+                out[i * Nout + n] = orc_f32_to_bf16(y);
+            }
+        }
+        free(avals);
+    }
+    free(bvals);
+}
+
+void orc_gemm_fwd(const uint8_t *xc, const uint8_t *xs, const float *xd,
+                  const uint16_t *X, int64_t M, int64_t K,
+                  const uint8_t *wc, const uint8_t *ws, const float *wd, int64_t N,
+                  const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                  const uint16_t *C, const int64_t *row_idx, int64_t n_rows, uint16_t *Y) {
+    (void)M;
+    assert(K % 16 == 0);
+    /* T = X A^T: P[j,k] = A[j*K + k];  L = T B^T: Q[n,j] = B[n*r + j] */
+    gemm_tn_rows(xc, xs, xd, K, wc, ws, wd, N, X, K, A, K, 1, B, r, 1, r, s, C, row_idx, n_rows, Y);
+}
+
+void orc_gemm_dgrad(const uint8_t *gc, const uint8_t *gs, const float *gd,
+                    const uint16_t *dY, int64_t M, int64_t N,
+                    const uint8_t *wc, const uint8_t *ws, const float *wd, int64_t K,
+                    const uint16_t *A, const uint16_t *B, int32_t r, float s,
+                    const uint16_t *C, const int64_t *row_idx, int64_t n_rows, uint16_t *dX) {
+    (void)M;
+    assert(N % 16 == 0);
+    /* T' = dY B: P[j,n] = B[n*r + j];  L' = T' A: Q[k,j] = A[j*K + k] */
+    gemm_tn_rows(gc, gs, gd, N, wc, ws, wd, K, dY, N, B, 1, r, A, 1, K, r, s, C, row_idx, n_rows, dX);
+}
