@@ -1,0 +1,185 @@
+/*
+ * pact.h -- libpact: the NVFP4 data flow through the frozen projections of a
+ * LoRA decoder layer (PACT), for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, and where the pages define it:
+ *  - NVFP4: every 16 E2M1 elements share one E4M3 block scale, about 4.5 bits
+ *    per element (simolm.com PACT blog post, section "FAQ", the question on
+ *    what NVFP4 is).  This library adds one FP32 scale per row (a second-level
+ *    scale the pages leave open).
+ *  - The seven frozen projections (q/k/v/o/gate/up/down) run as NVFP4 GEMMs
+ *    with FP32 accumulation and BF16 output, both in the forward pass and for
+ *    the input gradient (blog, section "Method", first bullet; arXiv abstract
+ *    of "PACT: NVFP4 Data-Flow LoRA Fine-Tuning on Consumer GPUs").
+ *  - Quantization is fused into the RMSNorm and SiLU-multiply kernels; the
+ *    quantized RMSNorm output is what the backward reuses; the SiLU-multiply
+ *    forward reads BF16 and also keeps NVFP4 copies of gate/up for backward
+ *    (blog "Method", second and fourth bullets; abstract).
+ *  - Forward and backward NVFP4 weight layouts are rebuilt, transposed and
+ *    re-quantized once, then cached (blog "Method", fourth bullet; abstract).
+ *  - LoRA adapters A, B stay BF16 and are never quantized (blog "Method",
+ *    closing paragraph); the LoRA update is h = W0 x + B A x (kongchang.com
+ *    PEFT explainer, LoRA low-rank math).
+ *
+ * Numerics (one result is admitted for every quantized output):
+ *  Row quantizer Q over a row x[0..L), L % 16 == 0:
+ *    A = max|x|; d = fl32(A / 2688); if d == 0 every code is a signed zero and
+ *    every scale 0; D = fl32(6 d); per block b: t = fl32(max|x_b| / D),
+ *    s_b = E4M3 round-to-nearest-even of t, clamped to 448; S = fl32(s_b d);
+ *    code = sign | E2M1 round-to-nearest-even of fl32(|x| / S), clamped to 6
+ *    (magnitude 0 when S == 0).  fl32 is one IEEE binary32 rounding.
+ *  GEMM: out = bf16( fl32(fl32(acc d_a[m]) d_b[n]) + fl32(s L) (+ C) ),
+ *    acc = FP32 sum of exact products of decoded operands (E2M1 x E4M3, exact
+ *    in FP16), L = sum_j T[m,j] Q[n,j] with T = LoRA-down product.  The
+ *    summation order is the kernel's own: GEMM outputs match a sequential
+ *    reference within |err| <= 2 BF16 ulp + 1e-3 max_row|ref| and a relative
+ *    Frobenius error <= 4e-3.  All quantized outputs are bit-exact.
+ *
+ * Layout of an NVFP4 tensor [rows, cols] (canonical, row-major, dense):
+ *    codes  [rows][cols/2] bytes, element 2j in the low nibble of byte j,
+ *           E2M1 code = sign(bit 3) | exponent(bits 2..1) | mantissa(bit 0);
+ *    scales [rows][cols/16] E4M3 (OCP "FN", bias 7) bytes, values 0x00..0x7E;
+ *    row_scale [rows] FP32.
+ * BF16 tensors are passed as raw uint16_t bit patterns, row-major with the
+ * given leading dimension (elements).
+ *
+ * Conventions for every entry point:
+ *  - Ownership: every pointer is caller-owned DEVICE memory (except the
+ *    pact_nvfp4 / pact_lora descriptor structs themselves, which are host
+ *    structs read during the call).  The library allocates and frees nothing
+ *    and never synchronizes; it keeps no mutable state.
+ *  - Ordering: all device work is enqueued on `stream` (a hipStream_t passed
+ *    as void*, NULL = default stream); calls return before it completes.
+ *  - Errors: arguments are validated first; on any failure the call returns
+ *    the status and enqueues nothing.  A launch failure reported by the HIP
+ *    runtime returns PACT_ERR_HIP.  Nothing is printed or thrown.
+ *  - Alignment: every device pointer must be 16-byte aligned, and leading
+ *    dimensions of BF16 tensors multiples of 8 elements (PACT_ERR_MISALIGNED).
+ *  - Inputs must be finite; non-finite inputs give unspecified outputs.
+ */
+#ifndef PACT_H
+#define PACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PACT_VERSION 1
+/* Longest row the fused quantizers accept (columns). */
+#define PACT_MAX_ROW 32768
+
+typedef enum {
+    PACT_OK = 0,
+    PACT_ERR_INVALID_ARG = 1,       /* null required pointer, negative size, bad rank */
+    PACT_ERR_UNSUPPORTED_SHAPE = 2, /* contraction/row length not a multiple of 16, too long */
+    PACT_ERR_MISALIGNED = 3,        /* pointer not 16-byte aligned or ld not a multiple of 8 */
+    PACT_ERR_WORKSPACE = 4,         /* workspace missing or smaller than required */
+    PACT_ERR_HIP = 5                /* the HIP runtime reported an error */
+} pact_status;
+
+/* An NVFP4 tensor in device memory (layout above).  rows, cols give its shape;
+ * cols % 16 == 0. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *row_scale;
+    int64_t rows;
+    int64_t cols;
+} pact_nvfp4;
+
+/* BF16 LoRA adapters of one projection with weight W [N][K]:
+ * A [r][K] and B [N][r] row-major BF16 bits in device memory; r = 0 (or a NULL
+ * descriptor) means frozen path only; scale multiplies the LoRA term. */
+typedef struct {
+    const uint16_t *A;
+    const uint16_t *B;
+    int32_t r;
+    float scale;
+} pact_lora;
+
+/* Version of this ABI (PACT_VERSION). */
+int pact_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char *pact_status_string(pact_status s);
+
+/* Row quantizer Q (blog "Method": NVFP4 operands for the frozen GEMMs; used
+ * for GEMM inputs that have no fused producer, e.g. incoming gradients).
+ * x [rows][cols] BF16 with leading dimension ld_x -> *out (out->rows == rows,
+ * out->cols == cols).  cols % 16 == 0, cols <= PACT_MAX_ROW. */
+pact_status pact_quantize_nvfp4(const uint16_t *x, int64_t ld_x, int64_t rows, int64_t cols,
+                                const pact_nvfp4 *out, void *stream);
+
+/* Fused RMSNorm -> quantize (blog "Method", second and fourth bullets):
+ * ss = sum x^2 (binary64), rstd = fl32(1 / sqrt(ss / cols + eps)) (binary64
+ * ops), y = bf16(fl32(fl32(x rstd) gamma)), yq = Q(y).
+ * x [rows][cols] (ld_x), gamma [cols], y [rows][cols] (ld_y; may be NULL),
+ * yq (required), rstd [rows] FP32 (may be NULL). */
+pact_status pact_rmsnorm_quant_nvfp4(const uint16_t *x, int64_t ld_x, const uint16_t *gamma,
+                                     float eps, int64_t rows, int64_t cols,
+                                     uint16_t *y, int64_t ld_y, const pact_nvfp4 *yq,
+                                     float *rstd, void *stream);
+
+/* Fused SiLU*mul -> quantize (blog "Method", second bullet; abstract):
+ * h = bf16(fl32(sigma32(g) u)) with sigma32(g) the correctly rounded binary32
+ * value of g / (1 + exp(-g)); hq = Q(h); gq = Q(g) and uq = Q(u) are the
+ * NVFP4 copies kept for backward.  g, u [rows][cols] (ld_g, ld_u), h (ld_h;
+ * may be NULL), hq required, gq and uq may each be NULL. */
+pact_status pact_silu_mul_quant_nvfp4(const uint16_t *g, int64_t ld_g, const uint16_t *u,
+                                      int64_t ld_u, int64_t rows, int64_t cols,
+                                      uint16_t *h, int64_t ld_h, const pact_nvfp4 *hq,
+                                      const pact_nvfp4 *gq, const pact_nvfp4 *uq,
+                                      void *stream);
+
+/* Workspace bytes pact_build_weight_layouts needs for a weight [N][K]. */
+size_t pact_build_weight_layouts_workspace(int64_t N, int64_t K);
+
+/* Cached weight layouts (blog "Method", fourth bullet): W_fwd = Q over the
+ * rows of W [N][K] (blocks along K); R = fl32(decode(W_fwd) * row_scale);
+ * W_bwd = Q over the rows of R^T [K][N] (blocks along N).  Pass W (BF16) to
+ * quantize it, or W = NULL and W_fwd_in = an already-quantized forward layout
+ * (e.g. calibrated offline), which is copied to W_fwd when the two differ.
+ * N % 16 == 0, K % 16 == 0, N <= PACT_MAX_ROW. */
+pact_status pact_build_weight_layouts(const uint16_t *W, const pact_nvfp4 *W_fwd_in,
+                                      int64_t N, int64_t K, const pact_nvfp4 *W_fwd,
+                                      const pact_nvfp4 *W_bwd, void *ws, size_t ws_bytes,
+                                      void *stream);
+
+/* Workspace bytes the GEMMs need for M rows, output width N, contraction K and
+ * LoRA rank r (0 when r == 0). */
+size_t pact_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* Forward NVFP4 GEMM of one frozen projection plus its BF16 LoRA term
+ * (blog "Method", first bullet and closing paragraph; PEFT explainer):
+ *   Y = bf16( d_x[m] d_w[n] (Xq . W_fwd^T)[m,n] + s (bf16(X A^T) B^T)[m,n] (+ C[m,n]) )
+ * Xq [M][K] NVFP4, X [M][K] BF16 (ld_x; only read when lora->r > 0),
+ * W_fwd [N][K] NVFP4, C [M][N] BF16 with leading dimension ld_y (may be NULL,
+ * may alias Y), Y [M][N] (ld_y).  K % 16 == 0. */
+pact_status pact_gemm_nvfp4_fwd(const pact_nvfp4 *Xq, const uint16_t *X, int64_t ld_x,
+                                const pact_nvfp4 *W_fwd, const pact_lora *lora,
+                                const uint16_t *C, uint16_t *Y, int64_t ld_y,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* Input-gradient NVFP4 GEMM on the cached transposed layout (blog "Method",
+ * first and fourth bullets):
+ *   dX = bf16( d_dy[m] d_wb[k] (dYq . W_bwd^T)[m,k] + s (bf16(dY B) A)[m,k] (+ C[m,k]) )
+ * dYq [M][N] NVFP4, dY [M][N] BF16 (ld_dy; only read when lora->r > 0),
+ * W_bwd [K][N] NVFP4 (from pact_build_weight_layouts), C [M][K] (ld_dx; may be
+ * NULL, may alias dX), dX [M][K] (ld_dx).  N % 16 == 0. */
+pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16_t *dY, int64_t ld_dy,
+                                  const pact_nvfp4 *W_bwd, const pact_lora *lora,
+                                  const uint16_t *C, uint16_t *dX, int64_t ld_dx,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* Diagnostic: out[i] = sigma32(g[i]) (the binary32 sigmoid-times-input the
+ * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
+ * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */
+pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PACT_H */

@@ -1,0 +1,159 @@
+// pact_device.h -- device-side building blocks shared by libpact's kernels:
+// BF16 <-> FP32, the NVFP4 block encoder (per-16 E4M3 scale, E2M1 codes) and
+// wavefront reductions.  gfx950 only.
+//
+// Format (simolm.com PACT blog, FAQ): 16 E2M1 elements share one E4M3 block
+// scale; this library adds one FP32 scale per row.  Encoding rule (the pages
+// leave it open; this is the reading the library implements):
+//   d = fl32(amax_row / 2688), D = fl32(6 d),
+//   block scale s = E4M3 round-to-nearest-even of fl32(amax_block / D), <= 448,
+//   S = fl32(s d), code = sign | E2M1 round-to-nearest-even of fl32(|x| / S).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pact {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even FP32 -> BF16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3 value of a scale byte (0x00..0x7E), exact, via the hardware decoder.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// E4M3 round-to-nearest-even of t >= 0, clamped to 448 (0x7E).  The hardware
+// encoder rounds to nearest even but turns values above 448 into NaN, so the
+// clamp happens first; t <= 448 never needs saturation after rounding.
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float t) {
+    t = fminf(t, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;
+}
+
+// E2M1 codes (round-to-nearest-even, saturating at 6, sign kept for zero) of
+// two FP32 quotients a, b (already |x|/S with the sign of x): low nibble = a.
+__device__ __forceinline__ uint32_t e2m1_encode2(float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// fl32(|x| / S) for x exactly representable in BF16 and S a binary32, with the
+// sign of x: |x| has at most 8 significant bits, so the exact quotient is never
+// within 2^-49 (relative) of a binary32 rounding midpoint; the binary64 product
+// |x| * RN64(1/S) is within 2^-52 of it and therefore rounds to the same
+// binary32 value.  rS = 1.0 / (double)S (correctly rounded binary64 divide).
+__device__ __forceinline__ float quot_bf16(float x, double rS) {
+    return (float)((double)x * rS);
+}
+
+// fl32(x / S) for any binary32 x: binary64 division rounds correctly, and
+// binary64 -> binary32 rounding of it is the correctly rounded binary32
+// quotient (53 >= 2*24 + 2).
+__device__ __forceinline__ float quot_f32(float x, float S) {
+    return (float)((double)x / (double)S);
+}
+
+// Per-row parameters of the quantizer.
+struct RowQ {
+    float d;   // row scale
+    float D;   // fl32(6 d)
+};
+
+__device__ __forceinline__ RowQ row_params(float amax) {
+    RowQ r;
+    r.d = amax / 2688.0f;  // correctly rounded binary32 division (HIP default)
+    r.D = 6.0f * r.d;
+    return r;
+}
+
+// Encode one block of 16 BF16-exact values v[0..15] (FP32 registers) given
+// its block amax and the row parameters.  Returns the 8 code bytes packed in
+// two dwords and the scale byte.  When d == 0 (all-zero row) every code is the
+// sign bit only and the scale byte is 0.
+template <bool kBF16Exact>
+__device__ __forceinline__ void encode_block16(const float v[16], float bamax, RowQ rq,
+                                               uint32_t &codes_lo, uint32_t &codes_hi,
+                                               uint32_t &scale_byte) {
+    uint32_t w[2] = {0u, 0u};
+    if (rq.d == 0.0f) {
+        scale_byte = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            w[j >> 3] |= ((__float_as_uint(v[j]) >> 31) << 3) << (4 * (j & 7));
+        codes_lo = w[0];
+        codes_hi = w[1];
+        return;
+    }
+    float t = bamax / rq.D;  // correctly rounded
+    uint32_t sb = e4m3_encode_sat(t);
+    scale_byte = sb;
+    float S = e4m3_to_f32(sb) * rq.d;
+    if (S == 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            w[j >> 3] |= ((__float_as_uint(v[j]) >> 31) << 3) << (4 * (j & 7));
+    } else if (kBF16Exact) {
+        double rS = 1.0 / (double)S;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            float qa = quot_bf16(v[j], rS), qb = quot_bf16(v[j + 1], rS);
+            w[j >> 3] |= e2m1_encode2(qa, qb) << (4 * (j & 7));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            float qa = quot_f32(v[j], S), qb = quot_f32(v[j + 1], S);
+            w[j >> 3] |= e2m1_encode2(qa, qb) << (4 * (j & 7));
+        }
+    }
+    codes_lo = w[0];
+    codes_hi = w[1];
+}
+
+// ---- wavefront reductions (64 lanes) --------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Error-free double-double accumulation: (s, c) += x.
+__device__ __forceinline__ void dd_add(double &s, double &c, double x) {
+    double t = s + x;
+    double bp = t - s;
+    double e = (s - (t - bp)) + (x - bp);
+    s = t;
+    c += e;
+}
+
+__device__ __forceinline__ void dd_add_dd(double &s, double &c, double s2, double c2) {
+    dd_add(s, c, s2);
+    c += c2;
+}
+
+__device__ __forceinline__ void wave_sum_dd(double &s, double &c) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        double s2 = __shfl_xor(s, off, 64);
+        double c2 = __shfl_xor(c, off, 64);
+        dd_add_dd(s, c, s2, c2);
+    }
+}
+
+}  // namespace pact

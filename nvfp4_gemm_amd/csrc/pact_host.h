@@ -1,0 +1,47 @@
+// pact_host.h -- host-side helpers shared by libpact's entry points:
+// argument validation and launch-error mapping.  Validation never touches the
+// device, so every error path can be exercised without a GPU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pact.h"
+
+namespace pact {
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Validate an NVFP4 descriptor of shape [rows][cols] (cols % 16 == 0).
+inline pact_status check_nvfp4(const pact_nvfp4 *q, int64_t rows, int64_t cols) {
+    if (!q || !q->codes || !q->scales || !q->row_scale) return PACT_ERR_INVALID_ARG;
+    if (q->rows != rows || q->cols != cols) return PACT_ERR_INVALID_ARG;
+    if (!aligned16(q->codes) || !aligned16(q->scales) || !aligned16(q->row_scale))
+        return PACT_ERR_MISALIGNED;
+    return PACT_OK;
+}
+
+// Validate a BF16 matrix pointer with leading dimension ld (elements).
+inline pact_status check_bf16(const void *p, int64_t ld, int64_t cols) {
+    if (!p) return PACT_ERR_INVALID_ARG;
+    if (ld < cols) return PACT_ERR_INVALID_ARG;
+    if (!aligned16(p) || (ld % 8) != 0) return PACT_ERR_MISALIGNED;
+    return PACT_OK;
+}
+
+inline pact_status launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? PACT_OK : PACT_ERR_HIP;
+}
+
+#define PACT_TRY(expr)                      \
+    do {                                    \
+        pact_status _s = (expr);            \
+        if (_s != PACT_OK) return _s;       \
+    } while (0)
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace pact

@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libpact (include/pact.h).
+
+Argument marshalling only: every step of the data flow runs in libpact's HIP
+kernels.  PyTorch supplies device memory (tensors) and the stream.  If the
+built library is missing the binding raises; there is no CPU fallback.
+
+BF16 tensors are ``torch.bfloat16`` CUDA tensors (row-major, last stride 1);
+NVFP4 tensors are :class:`NVFP4Tensor` (codes / scales / row_scale tensors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpact.so")
+_lib = None
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+
+
+class pact_nvfp4(ctypes.Structure):
+    _fields_ = [("codes", P), ("scales", P), ("row_scale", P), ("rows", I64), ("cols", I64)]
+
+
+class pact_lora(ctypes.Structure):
+    _fields_ = [("A", P), ("B", P), ("r", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+STATUS = {0: "PACT_OK", 1: "PACT_ERR_INVALID_ARG", 2: "PACT_ERR_UNSUPPORTED_SHAPE",
+          3: "PACT_ERR_MISALIGNED", 4: "PACT_ERR_WORKSPACE", 5: "PACT_ERR_HIP"}
+
+EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
+           "pact_rmsnorm_quant_nvfp4", "pact_silu_mul_quant_nvfp4",
+           "pact_build_weight_layouts_workspace", "pact_build_weight_layouts",
+           "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
+           "pact_debug_sigmoid32"]
+
+
+class PactError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib():
+    """Load libpact.so (built in-tree by nvfp4_gemm_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpact.so not built ({LIB_PATH}); run nvfp4_gemm_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        NV = ctypes.POINTER(pact_nvfp4)
+        LO = ctypes.POINTER(pact_lora)
+        st = ctypes.c_int
+        L.pact_version.restype = ctypes.c_int
+        L.pact_status_string.restype = ctypes.c_char_p
+        L.pact_status_string.argtypes = [ctypes.c_int]
+        L.pact_quantize_nvfp4.restype = st
+        L.pact_quantize_nvfp4.argtypes = [P, I64, I64, I64, NV, P]
+        L.pact_rmsnorm_quant_nvfp4.restype = st
+        L.pact_rmsnorm_quant_nvfp4.argtypes = [P, I64, P, ctypes.c_float, I64, I64, P, I64, NV, P, P]
+        L.pact_silu_mul_quant_nvfp4.restype = st
+        L.pact_silu_mul_quant_nvfp4.argtypes = [P, I64, P, I64, I64, I64, P, I64, NV, NV, NV, P]
+        L.pact_build_weight_layouts_workspace.restype = ctypes.c_size_t
+        L.pact_build_weight_layouts_workspace.argtypes = [I64, I64]
+        L.pact_build_weight_layouts.restype = st
+        L.pact_build_weight_layouts.argtypes = [P, NV, I64, I64, NV, NV, P, ctypes.c_size_t, P]
+        L.pact_gemm_workspace.restype = ctypes.c_size_t
+        L.pact_gemm_workspace.argtypes = [I64, I64, I64, ctypes.c_int32]
+        gemm_args = [NV, P, I64, NV, LO, P, P, I64, P, ctypes.c_size_t, P]
+        L.pact_gemm_nvfp4_fwd.restype = st
+        L.pact_gemm_nvfp4_fwd.argtypes = gemm_args
+        L.pact_gemm_nvfp4_dgrad.restype = st
+        L.pact_gemm_nvfp4_dgrad.argtypes = gemm_args
+        L.pact_debug_sigmoid32.restype = st
+        L.pact_debug_sigmoid32.argtypes = [P, P, I64, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PactError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ld(t):
+    assert t.dim() == 2 and t.stride(1) == 1, "row-major 2-D tensor expected"
+    return t.stride(0)
+
+
+@dataclass
+class NVFP4Tensor:
+    """codes uint8 [rows, cols/2], scales uint8 [rows, cols/16] (E4M3 bytes),
+    row_scale float32 [rows]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    row_scale: torch.Tensor
+
+    @property
+    def rows(self):
+        return self.codes.shape[0]
+
+    @property
+    def cols(self):
+        return self.codes.shape[1] * 2
+
+    @staticmethod
+    def empty(rows: int, cols: int, device="cuda"):
+        return NVFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                           torch.empty((rows, cols // 16), dtype=torch.uint8, device=device),
+                           torch.empty((rows,), dtype=torch.float32, device=device))
+
+    def desc(self):
+        return pact_nvfp4(self.codes.data_ptr(), self.scales.data_ptr(),
+                          self.row_scale.data_ptr(), self.rows, self.cols)
+
+    def nbytes(self):
+        return self.codes.numel() + self.scales.numel() + 4 * self.row_scale.numel()
+
+
+def _desc_ref(q):
+    return None if q is None else ctypes.byref(q.desc())
+
+
+def pact_version() -> int:
+    return int(lib().pact_version())
+
+
+def pact_status_string(s: int) -> str:
+    return lib().pact_status_string(s).decode()
+
+
+def pact_quantize_nvfp4(x: torch.Tensor, out: NVFP4Tensor | None = None, stream=None):
+    rows, cols = x.shape
+    out = out if out is not None else NVFP4Tensor.empty(rows, cols, x.device)
+    d = out.desc()
+    _check(lib().pact_quantize_nvfp4(_ptr(x), _ld(x), rows, cols, ctypes.byref(d), _stream(stream)),
+           "pact_quantize_nvfp4")
+    return out
+
+
+def pact_rmsnorm_quant_nvfp4(x, gamma, eps, y=None, yq=None, rstd=None, want_y=True,
+                             want_rstd=True, stream=None):
+    rows, cols = x.shape
+    if y is None and want_y:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+    if yq is None:
+        yq = NVFP4Tensor.empty(rows, cols, x.device)
+    if rstd is None and want_rstd:
+        rstd = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    d = yq.desc()
+    _check(lib().pact_rmsnorm_quant_nvfp4(_ptr(x), _ld(x), _ptr(gamma), float(eps), rows, cols,
+                                          _ptr(y), _ld(y) if y is not None else cols,
+                                          ctypes.byref(d), _ptr(rstd), _stream(stream)),
+           "pact_rmsnorm_quant_nvfp4")
+    return y, yq, rstd
+
+
+def pact_silu_mul_quant_nvfp4(g, u, h=None, hq=None, gq=None, uq=None, want_h=True,
+                              want_stash=True, stream=None):
+    rows, cols = g.shape
+    if h is None and want_h:
+        h = torch.empty((rows, cols), dtype=torch.bfloat16, device=g.device)
+    if hq is None:
+        hq = NVFP4Tensor.empty(rows, cols, g.device)
+    if want_stash:
+        gq = gq if gq is not None else NVFP4Tensor.empty(rows, cols, g.device)
+        uq = uq if uq is not None else NVFP4Tensor.empty(rows, cols, g.device)
+    dh, dg, du = hq.desc(), (gq.desc() if gq is not None else None), (uq.desc() if uq is not None else None)
+    _check(lib().pact_silu_mul_quant_nvfp4(
+        _ptr(g), _ld(g), _ptr(u), _ld(u), rows, cols, _ptr(h), _ld(h) if h is not None else cols,
+        ctypes.byref(dh), ctypes.byref(dg) if dg is not None else None,
+        ctypes.byref(du) if du is not None else None, _stream(stream)), "pact_silu_mul_quant_nvfp4")
+    return h, hq, gq, uq
+
+
+def pact_build_weight_layouts_workspace(N: int, K: int) -> int:
+    return int(lib().pact_build_weight_layouts_workspace(N, K))
+
+
+def pact_build_weight_layouts(W=None, W_fwd_in: NVFP4Tensor | None = None, N=None, K=None,
+                              W_fwd=None, W_bwd=None, ws=None, stream=None):
+    if W is not None:
+        N, K = W.shape
+        dev = W.device
+    else:
+        N, K = W_fwd_in.rows, W_fwd_in.cols
+        dev = W_fwd_in.codes.device
+    W_fwd = W_fwd if W_fwd is not None else NVFP4Tensor.empty(N, K, dev)
+    W_bwd = W_bwd if W_bwd is not None else NVFP4Tensor.empty(K, N, dev)
+    need = pact_build_weight_layouts_workspace(N, K)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    df, db = W_fwd.desc(), W_bwd.desc()
+    din = W_fwd_in.desc() if W_fwd_in is not None else None
+    _check(lib().pact_build_weight_layouts(_ptr(W), ctypes.byref(din) if din is not None else None,
+                                           N, K, ctypes.byref(df), ctypes.byref(db), _ptr(ws),
+                                           ws.numel(), _stream(stream)),
+           "pact_build_weight_layouts")
+    return W_fwd, W_bwd
+
+
+def pact_gemm_workspace(M: int, N: int, K: int, r: int) -> int:
+    return int(lib().pact_gemm_workspace(M, N, K, r))
+
+
+@dataclass
+class LoRA:
+    """BF16 adapters of one projection W [N, K]: A [r, K], B [N, r], scale."""
+    A: torch.Tensor
+    B: torch.Tensor
+    scale: float
+
+    @property
+    def r(self):
+        return self.A.shape[0]
+
+    def desc(self):
+        return pact_lora(self.A.data_ptr(), self.B.data_ptr(), self.r, float(self.scale))
+
+
+def _gemm(fn, name, aq, Xl, bq, lora, C, out, ws, stream):
+    M, Nout = aq.rows, bq.rows
+    if out is None:
+        out = torch.empty((M, Nout), dtype=torch.bfloat16, device=aq.codes.device)
+    r = lora.r if lora is not None else 0
+    if ws is None and r > 0:
+        need = pact_gemm_workspace(M, Nout, aq.cols, r)
+        ws = torch.empty((need,), dtype=torch.uint8, device=aq.codes.device)
+    da, db = aq.desc(), bq.desc()
+    dl = lora.desc() if lora is not None else None
+    _check(fn(ctypes.byref(da), _ptr(Xl), _ld(Xl) if Xl is not None else 0, ctypes.byref(db),
+              ctypes.byref(dl) if dl is not None else None, _ptr(C), _ptr(out), _ld(out), _ptr(ws),
+              ws.numel() if ws is not None else 0, _stream(stream)), name)
+    return out
+
+
+def pact_gemm_nvfp4_fwd(Xq: NVFP4Tensor, W_fwd: NVFP4Tensor, X=None, lora: LoRA | None = None,
+                        C=None, Y=None, ws=None, stream=None):
+    """Y = bf16(d_x d_w Xq.W_fwd^T + s bf16(X A^T) B^T (+ C))."""
+    return _gemm(lib().pact_gemm_nvfp4_fwd, "pact_gemm_nvfp4_fwd", Xq, X, W_fwd, lora, C, Y, ws,
+                 stream)
+
+
+def pact_gemm_nvfp4_dgrad(dYq: NVFP4Tensor, W_bwd: NVFP4Tensor, dY=None, lora: LoRA | None = None,
+                          C=None, dX=None, ws=None, stream=None):
+    """dX = bf16(d_dy d_wb dYq.W_bwd^T + s bf16(dY B) A (+ C))."""
+    return _gemm(lib().pact_gemm_nvfp4_dgrad, "pact_gemm_nvfp4_dgrad", dYq, dY, W_bwd, lora, C, dX,
+                 ws, stream)
+
+
+def pact_debug_sigmoid32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(g_bits.shape, dtype=torch.float32, device=g_bits.device)
+    _check(lib().pact_debug_sigmoid32(_ptr(g_bits), _ptr(out), g_bits.numel(), _stream(stream)),
+           "pact_debug_sigmoid32")
+    return out

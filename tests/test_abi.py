@@ -1,0 +1,119 @@
+"""The C ABI (include/pact.h): libpact.so loads, exports every declared entry
+point, and rejects bad arguments with the documented status before touching
+the device -- all checked on the host, without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_gemm_amd import pact as pb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pact.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pact_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pb.LIB_PATH):
+        from nvfp4_gemm_amd import build
+        build.build()
+    return pb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(pb.EXPORTS) == names
+
+
+def test_version_and_status_strings(L):
+    assert pb.pact_version() == 1
+    for code, name in pb.STATUS.items():
+        assert pb.pact_status_string(code) == name
+
+
+def _nv(codes=0x1000, scales=0x2000, d=0x3000, rows=4, cols=32):
+    return pb.pact_nvfp4(codes, scales, d, rows, cols)
+
+
+FAKE = 0x7f0000001000  # never dereferenced: validation fails before any device access
+
+
+def test_quantize_validation(L):
+    q = _nv(rows=4, cols=32)
+    s = None
+    assert L.pact_quantize_nvfp4(None, 32, 4, 32, ctypes.byref(q), s) == 1
+    assert L.pact_quantize_nvfp4(FAKE, 32, 4, 24, ctypes.byref(_nv(cols=24)), s) == 2
+    assert L.pact_quantize_nvfp4(FAKE, 32, -1, 32, ctypes.byref(q), s) == 1
+    assert L.pact_quantize_nvfp4(FAKE + 2, 32, 4, 32, ctypes.byref(q), s) == 3
+    assert L.pact_quantize_nvfp4(FAKE, 36, 4, 32, ctypes.byref(q), s) == 3   # ld % 8
+    assert L.pact_quantize_nvfp4(FAKE, 16, 4, 32, ctypes.byref(q), s) == 1   # ld < cols
+    assert L.pact_quantize_nvfp4(FAKE, 32, 4, 32, None, s) == 1
+    assert L.pact_quantize_nvfp4(FAKE, 32, 4, 32, ctypes.byref(_nv(rows=5)), s) == 1
+    assert L.pact_quantize_nvfp4(FAKE, 32, 4, 32, ctypes.byref(_nv(codes=0x1001)), s) == 3
+    big = 32768 + 16
+    assert L.pact_quantize_nvfp4(FAKE, big, 1, big, ctypes.byref(_nv(rows=1, cols=big)), s) == 2
+
+
+def test_rmsnorm_silu_validation(L):
+    q = _nv(rows=4, cols=32)
+    assert L.pact_rmsnorm_quant_nvfp4(FAKE, 32, None, 1e-5, 4, 32, None, 32, ctypes.byref(q), None, None) == 1
+    assert L.pact_rmsnorm_quant_nvfp4(FAKE, 32, FAKE, -1.0, 4, 32, None, 32, ctypes.byref(q), None, None) == 1
+    assert L.pact_rmsnorm_quant_nvfp4(FAKE, 32, FAKE, 1e-5, 4, 32, None, 32, None, None, None) == 1
+    assert L.pact_rmsnorm_quant_nvfp4(FAKE, 32, FAKE, 1e-5, 4, 32, None, 32, ctypes.byref(q), FAKE + 4, None) == 3
+    assert L.pact_silu_mul_quant_nvfp4(FAKE, 32, None, 32, 4, 32, None, 32, ctypes.byref(q), None, None, None) == 1
+    assert L.pact_silu_mul_quant_nvfp4(FAKE, 32, FAKE, 32, 4, 40, None, 40, ctypes.byref(_nv(cols=40)), None, None, None) == 2
+    assert L.pact_silu_mul_quant_nvfp4(FAKE, 32, FAKE, 32, 4, 32, None, 32, ctypes.byref(q),
+                                       ctypes.byref(_nv(rows=3)), None, None) == 1
+
+
+def test_layout_validation(L):
+    N, K = 32, 64
+    f, b = _nv(rows=N, cols=K), _nv(rows=K, cols=N)
+    need = L.pact_build_weight_layouts_workspace(N, K)
+    assert need >= 4 * K
+    args = (N, K, ctypes.byref(f), ctypes.byref(b))
+    assert L.pact_build_weight_layouts(None, None, *args, FAKE, need, None) == 1         # neither W nor W_fwd_in
+    assert L.pact_build_weight_layouts(FAKE, ctypes.byref(f), *args, FAKE, need, None) == 1  # both
+    assert L.pact_build_weight_layouts(FAKE, None, *args, None, 0, None) == 4
+    assert L.pact_build_weight_layouts(FAKE, None, *args, FAKE, need - 1, None) == 4
+    assert L.pact_build_weight_layouts(FAKE, None, 24, K, ctypes.byref(_nv(rows=24, cols=K)),
+                                       ctypes.byref(_nv(rows=K, cols=24)), FAKE, need, None) == 2
+    assert L.pact_build_weight_layouts(FAKE, None, N, K, ctypes.byref(f), ctypes.byref(_nv(rows=N, cols=K)),
+                                       FAKE, need, None) == 1  # backward layout must be [K][N]
+
+
+def test_gemm_validation(L):
+    M, N, K = 8, 32, 64
+    xq, wq = _nv(rows=M, cols=K), _nv(rows=N, cols=K)
+    assert L.pact_gemm_workspace(M, N, K, 0) == 0
+    need = L.pact_gemm_workspace(M, N, K, 16)
+    assert need >= 2 * 16 * (M + N + K)
+    fwd = L.pact_gemm_nvfp4_fwd
+    assert fwd(None, None, 0, ctypes.byref(wq), None, None, FAKE, N, None, 0, None) == 1
+    assert fwd(ctypes.byref(xq), None, 0, ctypes.byref(_nv(rows=N, cols=48)), None, None, FAKE, N, None, 0, None) == 1
+    assert fwd(ctypes.byref(_nv(rows=M, cols=40)), None, 0, ctypes.byref(_nv(rows=N, cols=40)), None, None,
+               FAKE, N, None, 0, None) == 2
+    assert fwd(ctypes.byref(xq), None, 0, ctypes.byref(wq), None, None, FAKE + 8, N, None, 0, None) == 3
+    assert fwd(ctypes.byref(xq), None, 0, ctypes.byref(wq), None, None, FAKE, N - 8, None, 0, None) == 1
+    lo = pb.pact_lora(FAKE, FAKE, 16, 2.0)
+    assert fwd(ctypes.byref(xq), None, K, ctypes.byref(wq), ctypes.byref(lo), None, FAKE, N, FAKE, need, None) == 1
+    assert fwd(ctypes.byref(xq), FAKE, K, ctypes.byref(wq), ctypes.byref(lo), None, FAKE, N, None, 0, None) == 4
+    assert fwd(ctypes.byref(xq), FAKE, K, ctypes.byref(wq), ctypes.byref(lo), None, FAKE, N, FAKE, need - 1, None) == 4
+    bad_rank = pb.pact_lora(FAKE, FAKE, -1, 2.0)
+    assert fwd(ctypes.byref(xq), FAKE, K, ctypes.byref(wq), ctypes.byref(bad_rank), None, FAKE, N, FAKE, need, None) == 1
+    nullA = pb.pact_lora(None, FAKE, 16, 2.0)
+    assert fwd(ctypes.byref(xq), FAKE, K, ctypes.byref(wq), ctypes.byref(nullA), None, FAKE, N, FAKE, need, None) == 1
+    dg = L.pact_gemm_nvfp4_dgrad
+    dyq, wb = _nv(rows=M, cols=N), _nv(rows=K, cols=N)
+    assert dg(ctypes.byref(dyq), None, 0, ctypes.byref(_nv(rows=K, cols=K)), None, None, FAKE, K, None, 0, None) == 1
+    assert dg(ctypes.byref(dyq), FAKE, N, ctypes.byref(wb), ctypes.byref(lo), None, FAKE, K, None, 0, None) == 4
