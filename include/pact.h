@@ -28,9 +28,11 @@
  *    s_b = E4M3 round-to-nearest-even of t, clamped to 448; S = fl32(s_b d);
  *    code = sign | E2M1 round-to-nearest-even of fl32(|x| / S), clamped to 6
  *    (magnitude 0 when S == 0).  fl32 is one IEEE binary32 rounding.
- *  GEMM: out = bf16( fl32(fl32(acc d_a[m]) d_b[n]) + fl32(s L) (+ C) ),
+ *  GEMM: out = bf16( fl32(fl32(acc d_a[m]) d_b[n]) + L (+ C) ),
  *    acc = FP32 sum of exact products of decoded operands (E2M1 x E4M3, exact
- *    in FP16), L = sum_j T[m,j] Q[n,j] with T = LoRA-down product.  The
+ *    in FP16), L = sum_j T[m,j] Q[n,j] with T = bf16(s P) and P the FP32
+ *    LoRA-down product; for a power-of-two s this is exactly s times the
+ *    same sum taken with T = bf16(P).  The
  *    summation order is the kernel's own: GEMM outputs match a sequential
  *    reference within |err| <= 2 BF16 ulp + 1e-3 max_row|ref| and a relative
  *    Frobenius error <= 4e-3.  All quantized outputs are bit-exact.
@@ -154,7 +156,7 @@ size_t pact_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /* Forward NVFP4 GEMM of one frozen projection plus its BF16 LoRA term
  * (blog "Method", first bullet and closing paragraph; PEFT explainer):
- *   Y = bf16( d_x[m] d_w[n] (Xq . W_fwd^T)[m,n] + s (bf16(X A^T) B^T)[m,n] (+ C[m,n]) )
+ *   Y = bf16( d_x[m] d_w[n] (Xq . W_fwd^T)[m,n] + (bf16(s X A^T) B^T)[m,n] (+ C[m,n]) )
  * Xq [M][K] NVFP4, X [M][K] BF16 (ld_x; only read when lora->r > 0),
  * W_fwd [N][K] NVFP4, C [M][N] BF16 with leading dimension ld_y (may be NULL,
  * may alias Y), Y [M][N] (ld_y).  K % 16 == 0. */
@@ -165,7 +167,7 @@ pact_status pact_gemm_nvfp4_fwd(const pact_nvfp4 *Xq, const uint16_t *X, int64_t
 
 /* Input-gradient NVFP4 GEMM on the cached transposed layout (blog "Method",
  * first and fourth bullets):
- *   dX = bf16( d_dy[m] d_wb[k] (dYq . W_bwd^T)[m,k] + s (bf16(dY B) A)[m,k] (+ C[m,k]) )
+ *   dX = bf16( d_dy[m] d_wb[k] (dYq . W_bwd^T)[m,k] + (bf16(s dY B) A)[m,k] (+ C[m,k]) )
  * dYq [M][N] NVFP4, dY [M][N] BF16 (ld_dy; only read when lora->r > 0),
  * W_bwd [K][N] NVFP4 (from pact_build_weight_layouts), C [M][K] (ld_dx; may be
  * NULL, may alias dX), dX [M][K] (ld_dx).  N % 16 == 0. */

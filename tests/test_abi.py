@@ -97,7 +97,7 @@ def test_gemm_validation(L):
     xq, wq = _nv(rows=M, cols=K), _nv(rows=N, cols=K)
     assert L.pact_gemm_workspace(M, N, K, 0) == 0
     need = L.pact_gemm_workspace(M, N, K, 16)
-    assert need >= 2 * 16 * (M + N + K)
+    assert need >= 2 * 16 * M  # T = bf16(s X A^T), [M][r] BF16
     fwd = L.pact_gemm_nvfp4_fwd
     assert fwd(None, None, 0, ctypes.byref(wq), None, None, FAKE, N, None, 0, None) == 1
     assert fwd(ctypes.byref(xq), None, 0, ctypes.byref(_nv(rows=N, cols=48)), None, None, FAKE, N, None, 0, None) == 1
