@@ -43,6 +43,7 @@ struct GemmArgs {
     const uint8_t *b_scales;
     const float *b_d;
     int M, N, K;
+    uint32_t a_bytes, b_bytes;  // code bytes of the A and B operands (below 4 GiB)
     const uint16_t *T;  // [M][rpad] LoRA-down product (BF16, zero beyond r) or nullptr
     const uint16_t *Qs;  // LoRA-up operand: Q(n, j) = Qs[n * q_sn + j * q_sj], j < r
     int64_t q_sn, q_sj;
@@ -59,6 +60,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void load_lds16(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_base, 16, 0, 0);
 }
+
+// Workgroup barrier ordering LDS only: waits for this wavefront's own LDS
+// operations, not for its outstanding global loads (__syncthreads would also
+// wait for those, exposing the latency of the stage loads in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Waits until this wavefront's global loads, including the direct-to-LDS
+// loads of a stage, have completed.
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Packed FP4 dword (8 codes) -> 8 FP16 values (exact E2M1 x E4M3 products).
 __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t sc) {
@@ -93,42 +105,78 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gsize;
 }
 
-// LDS layout (ROWS = BM + BN rows: the A tile's rows, then the B tile's):
-//   P[2]  packed stages of 128 K-elements:
-//         codes  [ROWS][64 B], the four 16-byte pieces of a row stored in
-//                XOR-swizzled order (slot p of row r holds piece p ^ (r & 3));
-//         scales [ROWS][8 B], the row's 8 E4M3 block scales of the stage;
-//   F[2]  FP16 phases of 32 K-elements in MFMA fragment order: for row group
-//         g (32 rows) and K16 step s, 64 lanes x 16 bytes, lane (r, h) holding
-//         K [16 s + 8 h, 16 s + 8 h + 8) of row r.
-// Global -> P: direct 16-byte loads, 4 lanes per row (64 contiguous bytes)
-// for codes, one 4-byte load per lane for scales.  P -> F: every thread owns
-// one row and decodes its 32 elements of the next phase (4 dwords: 4 FP4->FP16
-// converts and 4 packed FP16 multiplies each) while the MFMAs of the current
-// phase run; the wavefronts then read their fragments from F.
-template <int BM, int BN, int WGM, int WGN, bool KFULL>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
-    constexpr int NW = WGM * WGN;
-    constexpr int NT = 64 * NW;
-    constexpr int FM = BM / WGM / 32;  // 32x32 fragments per wave along M
-    constexpr int FN = BN / WGN / 32;
-    constexpr int ROWS = BM + BN;
-    static_assert(ROWS == NT, "one decoded row per thread");
-    static_assert(BM % 32 == 0 && BN % 32 == 0 && FM >= 1 && FN >= 1, "unsupported tile");
-    constexpr int PK = 128;                   // K per packed stage
-    constexpr int PCODE = ROWS * 64;
-    constexpr int PSTAGE = ROWS * 72;
-    constexpr int FPH = ROWS * 64;            // FP16 phase: ROWS x 32 x 2 B
-    constexpr int N_CODE_I = ROWS / 16;       // direct loads per packed stage
-    constexpr int N_SC_I = ROWS / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PSTAGE + 2 * FPH];
-    uint8_t *const P0 = lds;
-    uint8_t *const F0 = lds + 2 * PSTAGE;
+// Main kernel.  Every wavefront owns a 128 x 128 accumulator tile (4 x 4
+// fragments of 32 x 32, 256 FP32 per lane) and decodes its own MFMA operands
+// from the packed NVFP4 stage in LDS: per K16 step it converts 8 fragments
+// (4 of A, 4 of B; one code dword each, 8 VALU) for 16 MFMAs, 4 VALU per
+// MFMA, which the MFMA pipe hides.
+//
+// A workgroup is 4 wavefronts arranged WM x WN x WK: the output tile is
+// (128 WM) x (128 WN); the WK wavefronts at the same (i, j) split K into WK
+// contiguous ranges, and their partial tiles are summed through LDS at the
+// end.  The WM x WN wavefronts of one K range form a group that stages its
+// packed operands together.
+//
+// LDS of a group: NBUF buffers of one stage of 64 K-elements each,
+//   codes  [ROWS][32 B], ROWS = the tile's A rows then its B rows; the two
+//          16-byte halves of a row are swapped on rows with bit 3 set, so the
+//          16 rows read by 16 lanes fall on 16 distinct groups of banks;
+//   scales [ROWS][4 B], the row's 4 E4M3 block scales of the stage.
+// Inside a stage, K is assigned to MFMA operand slots by lane half, the same
+// way in both operands: lanes 32h .. 32h+31 take elements [32h, 32h + 32) of
+// the stage, 8 per K16 step, so a lane reads one 16-byte half-row and one
+// 2-byte pair of scales per fragment and stage.  (Any assignment shared by
+// A and B gives the same dot product; only the FP32 summation order moves.)
+//
+// Pipeline: stage s+1 is read into a second register set during stage s,
+// stage s+3 is loaded from global memory (direct 16- and 4-byte loads into
+// LDS) while stage s is consumed, and the decode of step t+1 is interleaved
+// with the MFMAs of step t.  A group with several wavefronts meets at one
+// barrier per stage; a single-wavefront group needs none.
+constexpr int kNBuf = 4;   // LDS stage buffers per group
+// Buffer descriptor word 3 for raw (untyped, unswizzled) byte access on gfx950.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kSK = 64;    // K per stage
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int WM, int WN, int WK>
+struct GemmShape {
+    static constexpr int G = WM * WN;  // wavefronts per group
+    static constexpr int BM = 128 * WM, BN = 128 * WN;
+    static constexpr int ROWS = BM + BN;
+    static constexpr int PCODE = ROWS * 32;
+    static constexpr int STAGE = ROWS * 36;
+    static constexpr int GROUP_BYTES = kNBuf * STAGE;
+    static constexpr int N_CODE_I = ROWS / 32;  // 1 KB loads per stage: 32 rows x 32 B
+    static constexpr int N_SC_I = ROWS / 64;    // 256 B loads per stage: 64 rows x 4 B
+    static constexpr int LPW = (N_CODE_I + N_SC_I) / G;  // loads per wavefront per stage
+    static constexpr int NQC = N_CODE_I / G;              // of which code loads
+    // partial-tile exchange: WK == 2: 8 fragments per wavefront;
+    // WK == 4: 8 fragment slots per wavefront per round (2 rounds)
+    static constexpr int RED_BYTES = WK == 1 ? 0 : 4 * 8 * 4096;
+    static constexpr int LDS_BYTES = WK * GROUP_BYTES > RED_BYTES ? WK * GROUP_BYTES : RED_BYTES;
+    static_assert(G * WK == 4, "four wavefronts");
+    static_assert(N_CODE_I % G == 0 && N_SC_I % G == 0, "loads split evenly");
+};
+
+template <int WM, int WN, int WK, bool KFULL>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+    using SH = GemmShape<WM, WN, WK>;
+    constexpr int G = SH::G, BM = SH::BM, BN = SH::BN, ROWS = SH::ROWS;
+    constexpr int PCODE = SH::PCODE, STAGE = SH::STAGE, LPW = SH::LPW, NQC = SH::NQC;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / G;  // K range
+    const int wi = wave % G;   // position in the group
+    const int wm = wi / WN, wn = wi % WN;
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = (p.N + BN - 1) / BN;
     int tm, tn;
@@ -136,53 +184,69 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
     const int nblk = K >> 4;
-    const int nst = (K + PK - 1) / PK;  // packed stages
-    const int nph = 4 * nst;            // FP16 phases (K32 each)
+    const int S = ((K + kSK - 1) / kSK) / WK;  // stages per group (the host makes it exact)
+    const int gs0 = grp * S;                    // first global stage of this group
+    uint8_t *const glds = lds + grp * SH::GROUP_BYTES;
 
-    float16_t acc[FM][FN];
+    // ---- per-wavefront load assignment: load q of a stage ----
+    // code load i (< N_CODE_I): rows 32 i + lane/2, half (lane & 1) of the
+    // row's 32 bytes; scale load j: row 64 j + lane, 4 bytes.  A load
+    // instruction reads rows of one operand only (32- and 64-row groups never
+    // straddle the A/B boundary; which operand is known at compile time), so
+    // it is a buffer load with that operand's descriptor, a 32-bit lane
+    // offset and the stage offset in a scalar register.  Rows past the end
+    // are clamped to the last row (their results are never stored).
+    constexpr int QA_CODE = BM / (32 * G);  // code loads q < QA_CODE read A
+    constexpr int QA_SC = BM / (64 * G);    // scale loads q - NQC < QA_SC read A
+    static_assert(BM % (64 * G) == 0, "operand of a load is static");
+    const __amdgpu_buffer_rsrc_t rs_ac =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.a_codes, (short)0, (int)(p.a_bytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_bc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.b_codes, (short)0, (int)(p.b_bytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_as =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.a_scales, (short)0, (int)(p.a_bytes >> 3), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_bs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.b_scales, (short)0, (int)(p.b_bytes >> 3), kRsrcWord3);
+    // stages past the group's last one are loaded through a descriptor with
+    // no records: nothing is fetched, and the main loop stays branch-free
+    const __amdgpu_buffer_rsrc_t rs_none =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.a_codes, (short)0, 0, kRsrcWord3);
+    const int gp = (lane & 1) ^ ((lane >> 4) & 1);  // half of its row a code-load lane carries
+    uint32_t loff[LPW];  // lane's byte offset in its operand at K = 0
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    // global row of tile row rr (rows past the end are clamped: their results
-    // are never stored)
-    // kernel arguments in registers (the lambdas below must not reload them)
-    const uint8_t *const a_codes = p.a_codes;
-    const uint8_t *const a_scales = p.a_scales;
-    const uint8_t *const b_codes = p.b_codes;
-    const uint8_t *const b_scales = p.b_scales;
-    const int Mrows = p.M, Nrows = p.N;
-    auto row_src = [=](int rr, const uint8_t *&codes, const uint8_t *&scales, int &grow) {
-        if (rr < BM) {
-            codes = a_codes;
-            scales = a_scales;
-            grow = min(m0 + rr, Mrows - 1);
+    for (int q = 0; q < LPW; ++q) {
+        if (q < NQC) {
+            const int rr = 32 * (wi + G * q) + (lane >> 1);
+            const int crow = q < QA_CODE ? min(m0 + rr, p.M - 1) : min(n0 + rr - BM, p.N - 1);
+            loff[q] = (uint32_t)crow * (uint32_t)(K >> 1) + 16u * (uint32_t)gp;
         } else {
-            codes = b_codes;
-            scales = b_scales;
-            grow = min(n0 + rr - BM, Nrows - 1);
+            const int rr = 64 * (wi + G * (q - NQC)) + lane;
+            const int crow = q - NQC < QA_SC ? min(m0 + rr, p.M - 1) : min(n0 + rr - BM, p.N - 1);
+            loff[q] = (uint32_t)crow * (uint32_t)nblk;
         }
+    }
+    auto ldst = [&](int q) {  // LDS offset of load q in a stage buffer (uniform)
+        return q < NQC ? (wi + G * q) * 1024 : PCODE + (wi + G * (q - NQC)) * 256;
     };
 
-    auto issue_stage = [&](int st, uint8_t *buf) {
-        const int k0 = st * PK;
-        for (int i = wave; i < N_CODE_I + N_SC_I; i += NW) {
-            const uint8_t *codes, *scales;
-            int grow;
-            if (i < N_CODE_I) {
-                const int rr = 16 * i + (lane >> 2);
-                row_src(rr, codes, scales, grow);
-                const int g = (lane & 3) ^ (rr & 3);  // global piece stored in this slot
-                const uint8_t *src = codes + (int64_t)grow * (K >> 1) + (k0 >> 1) + 16 * g;
-                uint8_t *dst = buf + 16 * i * 64;
+    // loads of local stage s into buffer s % kNBuf
+    auto issue_stage = [&](int s) {
+        uint8_t *const buf = glds + (s % kNBuf) * STAGE;
+        const int gstage = gs0 + s;
+        const bool live = s < S;
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) {
+            lds_void_t *const dst = (lds_void_t *)(buf + ldst(q));
+            if (q < NQC) {
                 if (KFULL) {
-                    load_lds16(src, dst);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(!live ? rs_none : q < QA_CODE ? rs_ac : rs_bc, dst, 16, (int)loff[q],
+                                                             gstage * (kSK / 2), 0, 0);
                 } else {
+                    // K not a multiple of the stage: 8-byte pieces (one block
+                    // of 16 codes each) inside K, zeros past it
+                    const uint8_t *src = (q < QA_CODE ? p.a_codes : p.b_codes) + loff[q] + gstage * (kSK / 2);
+                    const int kk = gstage * kSK + 32 * gp;
                     u32x4 v = {0u, 0u, 0u, 0u};
-                    const int kk = k0 + 32 * g;
                     if (kk < K) {
                         const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
                         v.x = lo.x;
@@ -193,184 +257,292 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
                         v.z = hi.x;
                         v.w = hi.y;
                     }
-                    *reinterpret_cast<u32x4 *>(dst + 16 * lane) = v;
+                    *reinterpret_cast<u32x4 *>(buf + ldst(q) + 16 * lane) = v;
                 }
             } else {
-                const int j = i - N_CODE_I;
-                const int rr = 32 * j + (lane >> 1);
-                row_src(rr, codes, scales, grow);
-                const uint8_t *src = scales + (int64_t)grow * nblk + (k0 >> 4) + 4 * (lane & 1);
-                uint8_t *dst = buf + PCODE + 32 * j * 8;
                 if (KFULL) {
-                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 4, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(!live ? rs_none : q - NQC < QA_SC ? rs_as : rs_bs, dst, 4, (int)loff[q],
+                                                             gstage * (kSK / 16), 0, 0);
                 } else {
+                    const uint8_t *src =
+                        (q - NQC < QA_SC ? p.a_scales : p.b_scales) + loff[q] + gstage * (kSK / 16);
+                    const int b0 = gstage * (kSK / 16);
                     uint32_t w = 0u;
+#pragma unroll
                     for (int b = 0; b < 4; ++b)
-                        if ((k0 >> 4) + 4 * (lane & 1) + b < nblk) w |= (uint32_t)src[b] << (8 * b);
-                    *reinterpret_cast<uint32_t *>(dst + 4 * lane) = w;
+                        if (b0 + b < nblk) w |= (uint32_t)src[b] << (8 * b);
+                    *reinterpret_cast<uint32_t *>(buf + ldst(q) + 4 * lane) = w;
                 }
             }
         }
     };
 
-    // decode of phase ph: this thread's row (tid) -> F[ph & 1]
-    const int drow = tid;
-    const int dgrp = drow >> 5, dlr = drow & 31;
-    uint8_t *const fbase_w = F0 + (((dgrp * 2) * 64 + dlr) << 4);
-    u32x4 pcodes;
-    uint32_t pscale;
-    auto read_packed = [&](int ph) {
-        const uint8_t *pb = P0 + ((ph >> 2) & 1) * PSTAGE;
-        const int j = ph & 3;
-        pcodes = *reinterpret_cast<const u32x4 *>(pb + drow * 64 + ((j ^ (drow & 3)) << 4));
-        pscale = *reinterpret_cast<const uint16_t *>(pb + PCODE + drow * 8 + 2 * j);
-    };
-    auto decode_dword = [&](int ph, int d, half2_t sp) {
-        const uint32_t w = d == 0 ? pcodes.x : d == 1 ? pcodes.y : d == 2 ? pcodes.z : pcodes.w;
-        half2_t sc;
-        sc[0] = sp[d >> 1];
-        sc[1] = sp[d >> 1];
-        const half8_t v = decode8(w, sc);
-        // step s = d >> 1, lane half h = d & 1
-        *reinterpret_cast<half8_t *>(fbase_w + (ph & 1) * FPH + (((d >> 1) * 64 + 32 * (d & 1)) << 4)) = v;
-    };
-
-    auto read_a = [&](int ph, int s, int f) {
-        return *reinterpret_cast<const half8_t *>(F0 + (ph & 1) * FPH + ((((wm * FM + f) * 2 + s) * 64 + lane) << 4));
-    };
-    auto read_b = [&](int ph, int s, int f) {
-        return *reinterpret_cast<const half8_t *>(
-            F0 + (ph & 1) * FPH + ((((BM / 32 + wn * FN + f) * 2 + s) * 64 + lane) << 4));
-    };
-
-    if (nph > 0) {
-        issue_stage(0, P0);
-        if (nst > 1) issue_stage(1, P0 + PSTAGE);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        read_packed(0);
-        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pscale, 1.0f, false);
+    // ---- fragment reads: this lane's row of fragment f (0..3: A, 4..7: B) ----
+    const int lr = lane & 31;
+    const int rd_code = lr * 32 + 16 * (h ^ ((lr >> 3) & 1));
+    const int rd_sc = PCODE + lr * 4 + 2 * h;
+    const int a_row0 = wm * 128, b_row0 = BM + wn * 128;
+    u32x4 P[2][8];
+    uint32_t SC[2][8];
+    half2_t SCH[2][8];
+    auto read_stage = [&](int s, u32x4 (&Pd)[8], uint32_t (&Sd)[8]) {
+        const uint8_t *buf = glds + (s % kNBuf) * STAGE;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) decode_dword(0, d, sp);
-    }
-    __syncthreads();
-
-    // Phase loop.  The decode of phase ph+1 is unconditional (after the last
-    // phase it decodes stale LDS into the unused buffer, harmlessly), so each
-    // K16 step is one basic block in which scheduling groups interleave every
-    // MFMA with a slice of the decode VALU and the LDS traffic.
-    for (int ph = 0; ph < nph; ++ph) {
-        if ((ph & 3) == 0 && ph > 0 && (ph >> 2) + 1 < nst)
-            issue_stage((ph >> 2) + 1, P0 + (((ph >> 2) + 1) & 1) * PSTAGE);
-        read_packed(ph + 1);
-        half8_t av[FM], bv[FN];
-#pragma unroll
-        for (int f = 0; f < FM; ++f) av[f] = read_a(ph, 0, f);
-#pragma unroll
-        for (int f = 0; f < FN; ++f) bv[f] = read_b(ph, 0, f);
-        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pscale, 1.0f, false);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            half8_t an[FM], bn[FN];
-            if (s == 0) {
-#pragma unroll
-                for (int f = 0; f < FM; ++f) an[f] = read_a(ph, 1, f);
-#pragma unroll
-                for (int f = 0; f < FN; ++f) bn[f] = read_b(ph, 1, f);
-            }
-            decode_dword(ph + 1, 2 * s, sp);
-            decode_dword(ph + 1, 2 * s + 1, sp);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[fm], bv[fn], acc[fm][fn], 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < FM * FN; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
-                if (i % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // 1 LDS write
-                if (s == 0 && i < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            }
-            if (s == 0) {
-#pragma unroll
-                for (int f = 0; f < FM; ++f) av[f] = an[f];
-#pragma unroll
-                for (int f = 0; f < FN; ++f) bv[f] = bn[f];
-            }
+        for (int f = 0; f < 8; ++f) {
+            const int row0 = f < 4 ? a_row0 + 32 * f : b_row0 + 32 * (f - 4);
+            Pd[f] = *reinterpret_cast<const u32x4 *>(buf + row0 * 32 + rd_code);
+            Sd[f] = *reinterpret_cast<const uint16_t *>(buf + row0 * 4 + rd_sc);
         }
-        if ((ph & 3) == 2) __builtin_amdgcn_s_waitcnt(0);  // stage (ph >> 2) + 1 has landed
-        __syncthreads();
+    };
+    // operands of K16 step t (0..3) of a stage held in registers
+    auto decode = [&](const u32x4 (&Pb)[8], const uint32_t (&Sb)[8], half2_t (&Hb)[8], int t,
+                      half8_t (&out)[8]) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            if (t == 0) Hb[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(Sb[f], 1.0f, false);
+            const uint32_t w = t == 0 ? Pb[f].x : t == 1 ? Pb[f].y : t == 2 ? Pb[f].z : Pb[f].w;
+            half2_t sc;
+            sc[0] = Hb[f][t >> 1];
+            sc[1] = Hb[f][t >> 1];
+            out[f] = decode8(w, sc);
+        }
+    };
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    half8_t cur[8];
+    if (S > 0) {
+        // stages 0-2 in flight (those past the end fetch nothing); wait for 0
+        issue_stage(0);
+        if (KFULL || S > 1) issue_stage(1);
+        if (KFULL || S > 2) issue_stage(2);
+        if (KFULL)
+            wait_vmcnt<2 * LPW>();
+        else
+            wait_global_loads();
+        if (G > 1 || !KFULL) lds_barrier();
+        read_stage(0, P[0], SC[0]);
+        decode(P[0], SC[0], SCH[0], 0, cur);
     }
+
+    // one stage; register set B holds it, set B^1 receives the next stage
+    auto stage = [&](auto Bc, int s) {
+        constexpr int B = decltype(Bc)::value;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t == 1) {
+                // stage s+1 has landed (stages s+1 and s+2 are in flight);
+                // every wavefront of the group is past stage s-1, so its
+                // buffer may take stage s+3.  No branch here: a branch would
+                // split the step into blocks the scheduler cannot interleave.
+                if (KFULL) {
+                    wait_vmcnt<LPW>();
+                    if (G > 1) lds_barrier();
+                    issue_stage(s + 3);
+                } else {
+                    wait_global_loads();
+                    lds_barrier();
+                    if (s + 3 < S) issue_stage(s + 3);
+                }
+                read_stage(s + 1, P[B ^ 1], SC[B ^ 1]);
+            }
+            half8_t nx[8];
+            if (t < 3)
+                decode(P[B], SC[B], SCH[B], t + 1, nx);
+            else
+                decode(P[B ^ 1], SC[B ^ 1], SCH[B ^ 1], 0, nx);
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < 4; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[fm], cur[4 + fn], acc[fm][fn], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+                if (t == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            }
+#pragma unroll
+            for (int f = 0; f < 8; ++f) cur[f] = nx[f];
+        }
+    };
+    // pairs of stages (register sets 0, 1), then a last even stage if S is odd
+    int s = 0;
+    for (; s + 1 < S; s += 2) {
+        stage(std::integral_constant<int, 0>(), s);
+        stage(std::integral_constant<int, 1>(), s + 1);
+    }
+    if (s < S) stage(std::integral_constant<int, 0>(), s);
+
+    // drain the stage loads still in flight (they write LDS)
+    wait_global_loads();
 
     // ---- epilogue: row scales, LoRA term, residual, BF16 store ----
-    const int h = lane >> 5;
-    // Per fragment: y = fl32(fl32(acc d_a[m]) d_b[n]) in place, then the LoRA
-    // term T_s . Q^T (T_s = bf16(s . X P^T) from the down kernel) is accumulated
-    // into y by one BF16 MFMA per 16 ranks, then C is added and y rounded.
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int mb = m0 + (wm * FM + fm) * 32;
-        float dxv[16];
+    // y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s . Q^T
+    // (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by
+    // one BF16 MFMA per 16 ranks, then C is added and y rounded.
+    auto store_frag = [&](float16_t &a, int mb, int nb) {
+        const int n = nb + lr;
+        const float dw = n < p.N ? p.b_d[n] : 0.0f;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const int m = mb + 8 * e4 + 4 * h;
+            float dx[4];
             if (m + 3 < p.M) {
                 const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
-                dxv[4 * e4] = v[0];
-                dxv[4 * e4 + 1] = v[1];
-                dxv[4 * e4 + 2] = v[2];
-                dxv[4 * e4 + 3] = v[3];
+                dx[0] = v[0];
+                dx[1] = v[1];
+                dx[2] = v[2];
+                dx[3] = v[3];
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dxv[4 * e4 + q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
+                for (int q = 0; q < 4; ++q) dx[q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float y = a[4 * e4 + q] * dx[q];
+                a[4 * e4 + q] = y * dw;
             }
         }
+        if (p.T) {
+            const int mr = min(mb + lr, p.M - 1);
+            const int nr = min(n, p.N - 1);
+            for (int kk = 0; kk < p.rpad; kk += 16) {
+                const u32x4 va = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + kk + 8 * h);
+                u32x4 vb;
+                const int j0 = kk + 8 * h;
+                if (p.q_sj == 1 && (p.r & 7) == 0) {
+                    vb = u32x4{0u, 0u, 0u, 0u};
+                    if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
+                } else {
+                    uint32_t w[4];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int nb = n0 + (wn * FN + fn) * 32;
-            const int n = nb + (lane & 31);
-            const float dw = n < p.N ? p.b_d[n] : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float y = acc[fm][fn][e] * dxv[e];
-                acc[fm][fn][e] = y * dw;
-            }
-            if (p.T) {
-                const int mr = min(mb + (lane & 31), p.M - 1);
-                const int nr = min(n, p.N - 1);
-                for (int kk = 0; kk < p.rpad; kk += 16) {
-                    const u32x4 va = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + kk + 8 * h);
-                    u32x4 vb;
-                    const int j0 = kk + 8 * h;
-                    if (p.q_sj == 1 && (p.r & 7) == 0) {
-                        vb = u32x4{0u, 0u, 0u, 0u};
-                        if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
-                    } else {
-                        uint32_t w[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int ja = j0 + 2 * e, jb = ja + 1;
-                            const uint32_t lo = ja < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)ja * p.q_sj] : 0u;
-                            const uint32_t hi = jb < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)jb * p.q_sj] : 0u;
-                            w[e] = lo | (hi << 16);
-                        }
-                        vb = u32x4{w[0], w[1], w[2], w[3]};
+                    for (int e = 0; e < 4; ++e) {
+                        const int ja = j0 + 2 * e, jb = ja + 1;
+                        const uint32_t lo = ja < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)ja * p.q_sj] : 0u;
+                        const uint32_t hi = jb < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)jb * p.q_sj] : 0u;
+                        w[e] = lo | (hi << 16);
                     }
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, vb), acc[fm][fn], 0, 0, 0);
+                    vb = u32x4{w[0], w[1], w[2], w[3]};
                 }
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                            __builtin_bit_cast(bf16x8_t, vb), a, 0, 0, 0);
             }
-            if (n >= p.N) continue;
+        }
+        if (n >= p.N) return;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m >= p.M) continue;
-                float y = acc[fm][fn][e];
-                const int64_t off = (int64_t)m * p.ldy + n;
-                if (p.C) y = y + bf16_to_f32(p.C[off]);
-                p.Y[off] = (uint16_t)f32_to_bf16_bits(y);
+        for (int e = 0; e < 16; ++e) {
+            const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (m >= p.M) continue;
+            float y = a[e];
+            const int64_t off = (int64_t)m * p.ldy + n;
+            if (p.C) y = y + bf16_to_f32(p.C[off]);
+            p.Y[off] = (uint16_t)f32_to_bf16_bits(y);
+        }
+    };
+    const int mw = m0 + a_row0, nw = n0 + wn * 128;
+
+    // partial fragment slot: [e4][lane][4 floats], 4 KB, conflict-free
+    auto put_frag = [&](uint8_t *slot, const float16_t &a) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            float4_t v = {a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
+            *reinterpret_cast<float4_t *>(slot + e4 * 1024 + lane * 16) = v;
+        }
+    };
+    auto get_frag = [&](const uint8_t *slot) {
+        float16_t a;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4_t v = *reinterpret_cast<const float4_t *>(slot + e4 * 1024 + lane * 16);
+            a[4 * e4] = v[0];
+            a[4 * e4 + 1] = v[1];
+            a[4 * e4 + 2] = v[2];
+            a[4 * e4 + 3] = v[3];
+        }
+        return a;
+    };
+
+    if constexpr (WK == 1) {
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn) store_frag(acc[fm][fn], mw + 32 * fm, nw + 32 * fn);
+    } else if constexpr (WK == 2) {
+        // group 0 keeps fragment rows 0-1, group 1 rows 2-3; each wavefront
+        // hands the other half to its partner (same position, other group).
+        // Sum order: group 0's partial + group 1's partial.
+        lds_barrier();
+        uint8_t *const mine = lds + wave * 8 * 4096;
+        const uint8_t *const other = lds + ((1 - grp) * G + wi) * 8 * 4096;
+        auto exchange = [&](auto Kc) {
+            constexpr int KEEP = decltype(Kc)::value;  // first kept fragment row
+            constexpr int GIVE = 2 - KEEP;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int fn = 0; fn < 4; ++fn) put_frag(mine + (i * 4 + fn) * 4096, acc[GIVE + i][fn]);
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int fn = 0; fn < 4; ++fn) {
+                    const float16_t o = get_frag(other + (i * 4 + fn) * 4096);
+                    float16_t &a = acc[KEEP + i][fn];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) a[e] = KEEP == 0 ? a[e] + o[e] : o[e] + a[e];
+                    store_frag(a, mw + 32 * (KEEP + i), nw + 32 * fn);
+                }
+        };
+        if (grp == 0)
+            exchange(std::integral_constant<int, 0>());
+        else
+            exchange(std::integral_constant<int, 2>());
+    } else {
+        // WK == 4: wavefront w keeps fragment row w.  Two rounds of two
+        // fragment columns; slot (q, fm, fn') of wavefront q at
+        // lds + ((q * 4 + fm) * 2 + fn') * 4 KB.  Sum order: wavefront 0, 1, 2, 3.
+        auto round = [&](auto Wc, int rnd) {
+            constexpr int W = decltype(Wc)::value;
+            lds_barrier();
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+                if (fm != W)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        put_frag(lds + ((W * 4 + fm) * 2 + j) * 4096, acc[fm][2 * rnd + j]);
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float16_t sum;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float16_t part = q == W ? acc[W][2 * rnd + j] : get_frag(lds + ((q * 4 + W) * 2 + j) * 4096);
+                    if (q == 0)
+                        sum = part;
+                    else
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) sum[e] = sum[e] + part[e];
+                }
+                store_frag(sum, mw + 32 * W, nw + 32 * (2 * rnd + j));
             }
+        };
+#pragma unroll
+        for (int rnd = 0; rnd < 2; ++rnd) {
+            if (wave == 0)
+                round(std::integral_constant<int, 0>(), rnd);
+            else if (wave == 1)
+                round(std::integral_constant<int, 1>(), rnd);
+            else if (wave == 2)
+                round(std::integral_constant<int, 2>(), rnd);
+            else
+                round(std::integral_constant<int, 3>(), rnd);
         }
     }
 }
@@ -442,22 +614,57 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     return (size_t)round_up(M * rpad * 2, 256);
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int WM, int WN, int WK>
 static void launch_gemm_cfg(const GemmArgs &a, hipStream_t st) {
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    const dim3 block(64 * WGM * WGN);
-    if (a.K % 128 == 0)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, true>), dim3(tiles), block, 0, st, a);
+    using SH = GemmShape<WM, WN, WK>;
+    const int tiles = ((a.M + SH::BM - 1) / SH::BM) * ((a.N + SH::BN - 1) / SH::BN);
+    if (a.K % kSK == 0)
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, true>), dim3(tiles), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, false>), dim3(tiles), block, 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, false>), dim3(tiles), dim3(256), 0, st, a);
 }
 
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Wavefront arrangement: the estimated duration is the number of rounds of
+// one workgroup per CU times a wavefront's share of K, plus the partial-sum
+// exchange (about one stage for a 2-way K split, one and a half for 4-way).
 static pact_status run_gemm(const GemmArgs &a, hipStream_t st) {
-    auto tiles = [&](int bm, int bn) {
-        return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    const int64_t ns = (a.K + kSK - 1) / kSK;
+    const int cus = device_cus();
+    struct Cand {
+        int wm, wn, wk;
     };
-    if (tiles(256, 256) >= 192) launch_gemm_cfg<256, 256, 2, 4>(a, st);
-    else launch_gemm_cfg<128, 128, 2, 2>(a, st);
+    const Cand cands[4] = {{2, 2, 1}, {2, 1, 2}, {1, 2, 2}, {1, 1, 4}};
+    int best = 0;
+    double best_cost = 0.0;
+    for (int c = 0; c < 4; ++c) {
+        const Cand &k = cands[c];
+        if (ns % k.wk != 0) continue;
+        const int64_t tiles = ((a.M + 128 * k.wm - 1) / (128 * k.wm)) * ((a.N + 128 * k.wn - 1) / (128 * k.wn));
+        const int64_t rounds = (tiles + cus - 1) / cus;
+        const double cost = (double)rounds * ((double)(ns / k.wk) + (k.wk == 2 ? 1.0 : k.wk == 4 ? 1.5 : 0.0));
+        if (c == 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    switch (best) {
+        case 0: launch_gemm_cfg<2, 2, 1>(a, st); break;
+        case 1: launch_gemm_cfg<2, 1, 2>(a, st); break;
+        case 2: launch_gemm_cfg<1, 2, 2>(a, st); break;
+        default: launch_gemm_cfg<1, 1, 4>(a, st); break;
+    }
     return launch_status();
 }
 
@@ -474,6 +681,9 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     if (M < 0 || Kc < 0 || Nout < 0 || bq->cols != Kc) return PACT_ERR_INVALID_ARG;
     if (Kc % 16 != 0) return PACT_ERR_UNSUPPORTED_SHAPE;
     if (M > INT32_MAX || Nout > INT32_MAX || Kc > INT32_MAX) return PACT_ERR_UNSUPPORTED_SHAPE;
+    // operand codes are addressed with 32-bit offsets
+    if (M * (Kc / 2) > (int64_t)UINT32_MAX || Nout * (Kc / 2) > (int64_t)UINT32_MAX)
+        return PACT_ERR_UNSUPPORTED_SHAPE;
     PACT_TRY(check_nvfp4(aq, M, Kc));
     PACT_TRY(check_nvfp4(bq, Nout, Kc));
     PACT_TRY(check_bf16(Y, ldy, Nout));
@@ -497,6 +707,8 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     a.M = (int)M;
     a.N = (int)Nout;
     a.K = (int)Kc;
+    a.a_bytes = (uint32_t)(M * (Kc / 2));
+    a.b_bytes = (uint32_t)(Nout * (Kc / 2));
     a.C = C;
     a.Y = Y;
     a.ldy = ldy;
