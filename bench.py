@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
-"""Benchmark of libpact's hot path on one MI355X: one decoder layer's frozen
-projections through the NVFP4 data flow, forward + input-gradient backward.
+"""Benchmark of libpact's hot path on one MI355X: the frozen projections of
+LoRA decoder layers through the NVFP4 data flow, forward + input-gradient
+backward (simolm.com PACT blog post, section "Method"; arXiv abstract of
+"PACT: NVFP4 Data-Flow LoRA Fine-Tuning on Consumer GPUs").
 
-One step (every call goes through the C ABI):
+One step of a layer (every call goes through the C ABI):
   forward:  n1, n1q, rstd1 = rmsnorm_quant(x)
             q, k, v = fwd GEMMs on n1q (+ LoRA on n1)
-            a := q (attention core is not part of the frozen path: identity
+            a := q (the attention core is not part of the frozen path: identity
             stand-in), aq = Q(a), x2 = fwd_o(aq, a, C = x)
             n2, n2q, rstd2 = rmsnorm_quant(x2); g, u = fwd GEMMs on n2q
             h, hq, gq, uq = silu_mul_quant(g, u); x' = fwd_down(hq, h, C = x2)
@@ -14,17 +16,28 @@ One step (every call goes through the C ABI):
             da = dgrad_o(Q(dx2), dx2); stand-ins dq = da, dk = da[:, :KV],
             dv = da[:, KV:2KV]
             dx = dgrad_v(Q(dv), dv, C = dgrad_k(Q(dk), dk, C = dgrad_q(Q(dq), dq, C = dx2)))
-Weights and both cached NVFP4 layouts are built once before timing.
+A stack runs the layers' forwards in order, keeping each layer's NVFP4 stash
+(n1q, aq, n2q, gq, uq, hq, rstd1, rstd2), then the backwards in reverse order.
+The single-linear workload is Q(X), fwd, Q(dY), dgrad.  Weights and both
+cached NVFP4 layouts are built once before timing.
 
 Prints ONE JSON line.  `value` = frozen-projection GEMM FLOPs of the step
-(2 M N K over the 7 forward and 7 input-gradient GEMMs) / wall time of the
-whole step (every kernel included), in TFLOP/s.
+(2 M N K over every forward and input-gradient GEMM) / wall time of the whole
+step (every kernel included), in TFLOP/s.
+
+Other modes (used to calibrate and summarize rocprofv3 counter runs):
+  --copy-calibration MIB   runs a plain device-to-device copy of MIB MiB
+  --summarize-pmc DIR ...  turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+                           databases into the HBM-traffic summary text
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import sqlite3
 import sys
 import time
 
@@ -37,6 +50,9 @@ METRIC = "NVFP4 frozen-proj GEMM TFLOP/s (fwd+dgrad) + layer tokens/s, % of roof
 PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
 PEAK_FP4_TFLOPS = 10100.0       # context only: scaled FP4 MFMA cannot apply per-16 E4M3 scales
 PEAK_HBM_GBS = 8000.0
+GEMM_SOURCE = os.path.join(ROOT, "nvfp4_gemm_amd", "csrc", "pact_gemm.hip")
+CONFIGS = ["single_linear", "llama1b_layer", "qwen1.5b_layer", "llama3b_layer", "llama3b_stack28"]
+GEMM_KERNELS = ("gemm_kernel", "lora_down_kernel")
 
 
 def parse():
@@ -44,123 +60,221 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="llama1b_layer",
-                    choices=["llama1b_layer", "qwen1.5b_layer", "llama3b_layer"])
+    ap.add_argument("--config", default="llama1b_layer", choices=CONFIGS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="tokens in the oracle sample (0: pick for ~10-20 s of CPU work)")
+                    help="tokens in the oracle sample (0: the whole batch, at most 1024)")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the cache-flushed timing of the memory-bound kernels")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB_DIR", "WRITE_DB_DIR", "COPY_FETCH_DIR",
+                                                         "COPY_WRITE_DIR"))
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--pmc-out", default="")
+    ap.add_argument("--pmc-command", default="")
     return ap.parse_args()
 
 
-class Layer:
-    """Device buffers and weights of one layer, plus the step schedule."""
+def nvb(rows, cols):
+    """Bytes of an NVFP4 tensor: codes + E4M3 block scales + FP32 row scales."""
+    return rows * cols * 9 // 16 + 4 * rows
 
-    def __init__(self, shape, seed):
+
+class Stack:
+    """Device buffers, weights and the step schedule of `layers` decoder layers."""
+
+    def __init__(self, shape, seed, layers):
         import torch
         from nvfp4_gemm_amd import pact as pb
         from nvfp4_gemm_amd import synth
-        self.pb, self.torch, self.S = pb, torch, shape
-        li = synth.layer_inputs(shape, seed=seed)
-        self.li = li
+        self.pb, self.torch, self.S, self.L = pb, torch, shape, layers
         dev = "cuda"
-        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        self.bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(
+            torch.bfloat16).to(dev)
         M, H, I, KV = shape.tokens, shape.hidden, shape.inter, shape.kv
         self.M, self.H, self.I, self.KV = M, H, I, KV
-        self.x, self.g1, self.g2, self.dout = bf(li.x), bf(li.gamma1), bf(li.gamma2), bf(li.dout)
         self.names = list(shape.projections().keys())
-        self.Wbf = {n: bf(li.W[n]) for n in self.names}
-        self.lora = {n: pb.LoRA(bf(li.A[n]), bf(li.B[n]), shape.lora_scale) for n in self.names}
         E = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=dev)
         Q = pb.NVFP4Tensor.empty
-        # forward activations
-        self.n1, self.n1q, self.rstd1 = E(M, H), Q(M, H), torch.empty(M, device=dev)
-        self.q, self.k, self.v = E(M, H), E(M, KV), E(M, KV)
-        self.aq, self.x2 = Q(M, H), E(M, H)
-        self.n2, self.n2q, self.rstd2 = E(M, H), Q(M, H), torch.empty(M, device=dev)
-        self.gt, self.up = E(M, I), E(M, I)
-        self.h, self.hq, self.gq, self.uq = E(M, I), Q(M, I), Q(M, I), Q(M, I)
-        self.xo = E(M, H)
-        # backward
+        self.Wf, self.Wb, self.lora, self.g1, self.g2 = [], [], [], [], []
+        self.layout_ms = 0.0
+        st = torch.cuda.current_stream()
+        for l in range(layers):
+            li = synth.layer_inputs(shape, seed=seed, layer=l)
+            if l == 0:
+                self.li0 = li
+                self.x0, self.dout = self.bf(li.x), self.bf(li.dout)
+            Wbf = {n: self.bf(li.W[n]) for n in self.names}
+            self.g1.append(self.bf(li.gamma1))
+            self.g2.append(self.bf(li.gamma2))
+            self.lora.append({n: pb.LoRA(self.bf(li.A[n]), self.bf(li.B[n]), shape.lora_scale)
+                              for n in self.names})
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            lay = {n: pb.pact_build_weight_layouts(Wbf[n]) for n in self.names}
+            e1.record(st)
+            torch.cuda.synchronize()
+            self.layout_ms += e0.elapsed_time(e1)
+            self.Wf.append({n: lay[n][0] for n in self.names})
+            self.Wb.append({n: lay[n][1] for n in self.names})
+            del Wbf, lay
+        # per-layer stash (kept from the forward to the backward)
+        self.stash = [dict(n1q=Q(M, H), rstd1=torch.empty(M, device=dev), aq=Q(M, H), n2q=Q(M, H),
+                           rstd2=torch.empty(M, device=dev), gq=Q(M, I), uq=Q(M, I), hq=Q(M, I))
+                      for _ in range(layers)]
+        # transient activations, shared by the layers
+        self.xs = [self.x0, E(M, H), E(M, H)]    # layer input / output ping-pong (x0 is kept)
+        self.n1, self.q, self.k, self.v = E(M, H), E(M, H), E(M, KV), E(M, KV)
+        self.x2, self.n2 = E(M, H), E(M, H)
+        self.gt, self.up, self.h = E(M, I), E(M, I), E(M, I)
         self.doq, self.dh, self.dhq = Q(M, H), E(M, I), Q(M, I)
         self.dx2, self.dx2q, self.da = E(M, H), Q(M, H), E(M, H)
-        self.dqq, self.dkq, self.dvq, self.dx = Q(M, H), Q(M, KV), Q(M, KV), E(M, H)
+        self.dqq, self.dkq, self.dvq = Q(M, H), Q(M, KV), Q(M, KV)
+        self.dxs = [self.dout, E(M, H), E(M, H)]
         need = max(pb.pact_gemm_workspace(M, n, k, shape.rank) for n, k in shape.projections().values())
-        self.ws = torch.empty((need,), dtype=torch.uint8, device=dev)
-        self.Wf, self.Wb = {}, {}
-
-    def build_layouts(self):
-        pb = self.pb
-        for n in self.names:
-            self.Wf[n], self.Wb[n] = pb.pact_build_weight_layouts(self.Wbf[n])
+        self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
 
     def calls(self):
-        """The step as a list of (kind, flops, bytes, fn)."""
+        """The step as a list of (kind, frozen flops, bytes, fn, lora flops)."""
         pb, S = self.pb, self.S
         M, H, I, KV, r = self.M, self.H, self.I, self.KV, S.rank
-        L, Wf, Wb, ws = self.lora, self.Wf, self.Wb, self.ws
+        ws = self.ws
         gemm_fl = lambda n, k: 2 * M * n * k
         lora_fl = lambda n, k: 2 * M * r * (n + k)
-        nvb = lambda rows, cols: rows * cols * 9 // 16 + 4 * rows
         c = []
-        c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
-                  lambda: pb.pact_rmsnorm_quant_nvfp4(self.x, self.g1, S.eps, self.n1, self.n1q, self.rstd1)))
-        for nm, out in (("q", self.q), ("k", self.k), ("v", self.v)):
-            n, k = S.projections()[nm]
-            c.append(("gemm_fwd", gemm_fl(n, k), 0, (lambda nm=nm, out=out: pb.pact_gemm_nvfp4_fwd(
-                self.n1q, Wf[nm], X=self.n1, lora=L[nm], Y=out, ws=ws)), lora_fl(n, k)))
-        c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(self.q, self.aq)))
-        c.append(("gemm_fwd", gemm_fl(H, H), 0, lambda: pb.pact_gemm_nvfp4_fwd(
-            self.aq, Wf["o"], X=self.q, lora=L["o"], C=self.x, Y=self.x2, ws=ws), lora_fl(H, H)))
-        c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
-                  lambda: pb.pact_rmsnorm_quant_nvfp4(self.x2, self.g2, S.eps, self.n2, self.n2q, self.rstd2)))
-        for nm, out in (("gate", self.gt), ("up", self.up)):
-            c.append(("gemm_fwd", gemm_fl(I, H), 0, (lambda nm=nm, out=out: pb.pact_gemm_nvfp4_fwd(
-                self.n2q, Wf[nm], X=self.n2, lora=L[nm], Y=out, ws=ws)), lora_fl(I, H)))
-        c.append(("silu_mul_quant", 0, M * I * 2 * 3 + 3 * nvb(M, I),
-                  lambda: pb.pact_silu_mul_quant_nvfp4(self.gt, self.up, self.h, self.hq, self.gq, self.uq)))
-        c.append(("gemm_fwd", gemm_fl(H, I), 0, lambda: pb.pact_gemm_nvfp4_fwd(
-            self.hq, Wf["down"], X=self.h, lora=L["down"], C=self.x2, Y=self.xo, ws=ws), lora_fl(H, I)))
-        # backward (input gradients)
-        c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(self.dout, self.doq)))
-        c.append(("gemm_dgrad", gemm_fl(H, I), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.doq, Wb["down"], dY=self.dout, lora=L["down"], dX=self.dh, ws=ws), lora_fl(H, I)))
-        c.append(("quantize", 0, M * I * 2 + nvb(M, I), lambda: pb.pact_quantize_nvfp4(self.dh, self.dhq)))
-        c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dhq, Wb["gate"], dY=self.dh, lora=L["gate"], C=self.dout, dX=self.dx2, ws=ws), lora_fl(I, H)))
-        c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dhq, Wb["up"], dY=self.dh, lora=L["up"], C=self.dx2, dX=self.dx2, ws=ws), lora_fl(I, H)))
-        c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(self.dx2, self.dx2q)))
-        c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dx2q, Wb["o"], dY=self.dx2, lora=L["o"], dX=self.da, ws=ws), lora_fl(H, H)))
-        dq, dk, dv = self.da, self.da[:, :KV], self.da[:, KV:2 * KV]
-        c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(dq, self.dqq)))
-        c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda: pb.pact_quantize_nvfp4(dk, self.dkq)))
-        c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda: pb.pact_quantize_nvfp4(dv, self.dvq)))
-        c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dqq, Wb["q"], dY=dq, lora=L["q"], C=self.dx2, dX=self.dx, ws=ws), lora_fl(H, H)))
-        c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dkq, Wb["k"], dY=dk, lora=L["k"], C=self.dx, dX=self.dx, ws=ws), lora_fl(KV, H)))
-        c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda: pb.pact_gemm_nvfp4_dgrad(
-            self.dvq, Wb["v"], dY=dv, lora=L["v"], C=self.dx, dX=self.dx, ws=ws), lora_fl(KV, H)))
-        return [(t[0], t[1], t[2], t[3], t[4] if len(t) > 4 else 0) for t in c]
+        xin = lambda l: self.xs[0] if l == 0 else self.xs[1 + (l - 1) % 2]
+        xout = lambda l: self.xs[1 + l % 2]
+        for l in range(self.L):
+            st, L, Wf = self.stash[l], self.lora[l], self.Wf[l]
+            x, xo = xin(l), xout(l)
+            c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
+                      lambda x=x, st=st, l=l: pb.pact_rmsnorm_quant_nvfp4(x, self.g1[l], S.eps, self.n1,
+                                                                          st["n1q"], st["rstd1"]), 0))
+            for nm, out in (("q", self.q), ("k", self.k), ("v", self.v)):
+                n, k = S.projections()[nm]
+                c.append(("gemm_fwd", gemm_fl(n, k), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
+                          pb.pact_gemm_nvfp4_fwd(st["n1q"], Wf[nm], X=self.n1, lora=L[nm], Y=out, ws=ws)),
+                          lora_fl(n, k)))
+            c.append(("quantize", 0, M * H * 2 + nvb(M, H),
+                      lambda st=st: pb.pact_quantize_nvfp4(self.q, st["aq"]), 0))
+            c.append(("gemm_fwd", gemm_fl(H, H), 0, lambda x=x, st=st, L=L, Wf=Wf: pb.pact_gemm_nvfp4_fwd(
+                st["aq"], Wf["o"], X=self.q, lora=L["o"], C=x, Y=self.x2, ws=ws), lora_fl(H, H)))
+            c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
+                      lambda st=st, l=l: pb.pact_rmsnorm_quant_nvfp4(self.x2, self.g2[l], S.eps, self.n2,
+                                                                     st["n2q"], st["rstd2"]), 0))
+            for nm, out in (("gate", self.gt), ("up", self.up)):
+                c.append(("gemm_fwd", gemm_fl(I, H), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
+                          pb.pact_gemm_nvfp4_fwd(st["n2q"], Wf[nm], X=self.n2, lora=L[nm], Y=out, ws=ws)),
+                          lora_fl(I, H)))
+            c.append(("silu_mul_quant", 0, M * I * 2 * 3 + 3 * nvb(M, I),
+                      lambda st=st: pb.pact_silu_mul_quant_nvfp4(self.gt, self.up, self.h, st["hq"], st["gq"],
+                                                                 st["uq"]), 0))
+            c.append(("gemm_fwd", gemm_fl(H, I), 0, lambda xo=xo, st=st, L=L, Wf=Wf: pb.pact_gemm_nvfp4_fwd(
+                st["hq"], Wf["down"], X=self.h, lora=L["down"], C=self.x2, Y=xo, ws=ws), lora_fl(H, I)))
+        # backward (input gradients), last layer first
+        for j, l in enumerate(reversed(range(self.L))):
+            L, Wb = self.lora[l], self.Wb[l]
+            dout = self.dxs[0] if j == 0 else self.dxs[1 + (j - 1) % 2]
+            dx = self.dxs[1 + j % 2]
+            c.append(("quantize", 0, M * H * 2 + nvb(M, H),
+                      lambda dout=dout: pb.pact_quantize_nvfp4(dout, self.doq), 0))
+            c.append(("gemm_dgrad", gemm_fl(H, I), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.doq, Wb["down"], dY=dout, lora=L["down"], dX=self.dh, ws=ws), lora_fl(H, I)))
+            c.append(("quantize", 0, M * I * 2 + nvb(M, I), lambda: pb.pact_quantize_nvfp4(self.dh, self.dhq), 0))
+            c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dhq, Wb["gate"], dY=self.dh, lora=L["gate"], C=dout, dX=self.dx2, ws=ws), lora_fl(I, H)))
+            c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dhq, Wb["up"], dY=self.dh, lora=L["up"], C=self.dx2, dX=self.dx2, ws=ws), lora_fl(I, H)))
+            c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(self.dx2, self.dx2q), 0))
+            c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dx2q, Wb["o"], dY=self.dx2, lora=L["o"], dX=self.da, ws=ws), lora_fl(H, H)))
+            dq, dk, dv = self.da, self.da[:, :KV], self.da[:, KV:2 * KV]
+            c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda dq=dq: pb.pact_quantize_nvfp4(dq, self.dqq), 0))
+            c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dk=dk: pb.pact_quantize_nvfp4(dk, self.dkq), 0))
+            c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dv=dv: pb.pact_quantize_nvfp4(dv, self.dvq), 0))
+            c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda dq=dq, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dqq, Wb["q"], dY=dq, lora=L["q"], C=self.dx2, dX=dx, ws=ws), lora_fl(H, H)))
+            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dk=dk, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dkq, Wb["k"], dY=dk, lora=L["k"], C=dx, dX=dx, ws=ws), lora_fl(KV, H)))
+            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dvq, Wb["v"], dY=dv, lora=L["v"], C=dx, dX=dx, ws=ws), lora_fl(KV, H)))
+        return c
 
     def stash_bytes(self):
+        """NVFP4 stash of the layers vs the BF16 stash the same frozen path keeps
+        under BF16 LoRA ({x, n1, attn_out, x2, n2} [M,H] and {g, u, h} [M,I],
+        plus the two FP32 rstd rows)."""
         M, H, I = self.M, self.H, self.I
-        nv = lambda q: q.nbytes()
-        pact = nv(self.n1q) + nv(self.aq) + nv(self.n2q) + nv(self.gq) + nv(self.uq) + nv(self.hq) + 8 * M
-        bf16 = 2 * (5 * M * H + 3 * M * I) + 8 * M
+        pact = sum(sum(v.nbytes() for k, v in st.items() if k.endswith("q")) + 8 * M for st in self.stash)
+        bf16 = self.L * (2 * (5 * M * H + 3 * M * I) + 8 * M)
         return pact, bf16
 
+    def config(self):
+        S = self.S
+        return {"workload": S.name, "layers": self.L, "tokens": S.tokens, "hidden": S.hidden,
+                "intermediate": S.inter, "kv": S.kv, "lora_rank": S.rank, "lora_scale": S.lora_scale,
+                "step": "forward + input-gradient backward of every layer, 7 frozen NVFP4 projections "
+                        "per layer with BF16 LoRA, fused RMSNorm/SiLU quantizers"}
 
-def cpu_baseline(S, li, sample_tokens):
-    """The oracle, as it stands, on the first `sample_tokens` tokens of the same
-    layer (every step of the data flow is per token, so this is the same
-    computation on a smaller batch)."""
+
+class Linear:
+    """The single NVFP4 LoRA linear: Q(X), fwd, Q(dY), dgrad."""
+
+    def __init__(self, seed):
+        import torch
+        from nvfp4_gemm_amd import pact as pb
+        from nvfp4_gemm_amd import synth
+        p = synth.SINGLE_LINEAR
+        self.pb, self.p = pb, p
+        li = synth.single_linear_inputs(M=p["M"], N=p["N"], K=p["K"], r=p["r"], s=p["lora_scale"], seed=seed)
+        self.li = li
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        self.X, self.dY, W = bf(li.X), bf(li.dY), bf(li.W)
+        self.lora = pb.LoRA(bf(li.A), bf(li.B), li.s)
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        self.Wf, self.Wb = pb.pact_build_weight_layouts(W)
+        e1.record(st)
+        torch.cuda.synchronize()
+        self.layout_ms = e0.elapsed_time(e1)
+        M, N, K = p["M"], p["N"], p["K"]
+        self.xq, self.dyq = pb.NVFP4Tensor.empty(M, K), pb.NVFP4Tensor.empty(M, N)
+        self.Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        self.dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        self.ws = torch.empty((max(pb.pact_gemm_workspace(M, N, K, p["r"]), 16),), dtype=torch.uint8,
+                              device="cuda")
+        self.M, self.N, self.K, self.L = M, N, K, 1
+
+    def calls(self):
+        pb, M, N, K, r = self.pb, self.M, self.N, self.K, self.p["r"]
+        return [
+            ("quantize", 0, M * K * 2 + nvb(M, K), lambda: pb.pact_quantize_nvfp4(self.X, self.xq), 0),
+            ("gemm_fwd", 2 * M * N * K, 0, lambda: pb.pact_gemm_nvfp4_fwd(
+                self.xq, self.Wf, X=self.X, lora=self.lora, Y=self.Y, ws=self.ws), 2 * M * r * (N + K)),
+            ("quantize", 0, M * N * 2 + nvb(M, N), lambda: pb.pact_quantize_nvfp4(self.dY, self.dyq), 0),
+            ("gemm_dgrad", 2 * M * N * K, 0, lambda: pb.pact_gemm_nvfp4_dgrad(
+                self.dyq, self.Wb, dY=self.dY, lora=self.lora, dX=self.dX, ws=self.ws), 2 * M * r * (N + K)),
+        ]
+
+    def stash_bytes(self):
+        return None
+
+    def config(self):
+        p = self.p
+        return {"workload": p["name"], "tokens": p["M"], "N": p["N"], "K": p["K"], "lora_rank": p["r"],
+                "lora_scale": p["lora_scale"], "step": "Q(X), forward GEMM, Q(dY), input-gradient GEMM"}
+
+
+def cpu_baseline_layer(S, li, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of one
+    layer of the same workload (every step of the data flow is per token, so
+    this is the same computation on a smaller batch)."""
     import oracle
     names = list(S.projections().keys())
     rows = np.arange(sample_tokens)
-    H, KV = S.hidden, S.kv
+    KV = S.kv
     t0 = time.perf_counter()
     Wf, Wb = {}, {}
     for n in names:
@@ -193,33 +307,184 @@ def cpu_baseline(S, li, sample_tokens):
     flops = 2 * sum(2 * sample_tokens * n * k for n, k in S.projections().values())
     return {"value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{sample_tokens} of {S.tokens} tokens through the full layer step "
-                      f"(fwd + input-gradient, all 14 GEMMs, quantizers, norms); weight layouts "
+            "sample": f"{sample_tokens} of {S.tokens} tokens through one full layer step "
+                      f"(fwd + input-gradient: 14 GEMMs with LoRA, quantizers, norms); weight layouts "
                       f"built once outside the timed part ({t_layout:.1f} s)",
             "seconds": t_step, "tokens_per_s": sample_tokens / t_step}
 
 
+def cpu_baseline_linear(lin):
+    import oracle
+    li, s = lin.li, lin.li.s
+    wf, wb = oracle.build_weight_layouts(li.W)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        xq = oracle.quantize_bf16(li.X)
+        oracle.gemm_fwd(xq, li.X, wf, li.A, li.B, s)
+        dyq = oracle.quantize_bf16(li.dY)
+        oracle.gemm_dgrad(dyq, li.dY, wb, li.A, li.B, s)
+        reps += 1
+        if time.perf_counter() - t0 > 5.0:
+            break
+    t_step = (time.perf_counter() - t0) / reps
+    flops = 2 * 2 * lin.M * lin.N * lin.K
+    return {"value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"the whole step, repeated {reps} times",
+            "seconds": t_step * reps, "tokens_per_s": lin.M / t_step}
+
+
+def isolated_timing(torch, calls, reps=10):
+    """Cache-flushed timing of the memory-bound kernels: for the largest call
+    of each kind, each repetition first overwrites a 512 MiB buffer (larger
+    than the 256 MB Infinity Cache) with a fill kernel, then times the call
+    alone with events on its stream.  Reports the median."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+    out = {}
+    for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant"):
+        cs = [c for c in calls if c[0] == kind]
+        if not cs:
+            continue
+        c = max(cs, key=lambda c: c[2])
+        ts = []
+        for _ in range(reps + 1):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            c[3]()
+            b.record(st)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts[1:]))
+        gbs = c[2] / (ms * 1e-3) / 1e9
+        out[kind] = {"bytes": c[2], "median_us": ms * 1e3, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    del flush
+    return out
+
+
+def gemm_source_sha():
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_summary(workload):
+    """HBM bytes per GEMM launch from the committed counter summary, when it
+    was taken on the current GEMM source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"gemm_hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256") != gemm_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_gemm_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for calibrating the traffic counters."""
+    import torch
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}), flush=True)
+
+
+def _pmc_rows(d, counter):
+    dbs = glob.glob(os.path.join(d, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    con = sqlite3.connect(dbs[0])
+    return con.execute("select name, dispatch_id, counter_value from pmc_events where counter_name = ?",
+                       (counter,)).fetchall()
+
+
+def summarize_pmc(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch, summed over the device) of
+    the GEMM kernels, scaled by what the same counters read for the copy."""
+    fdir, wdir, cfdir, cwdir = args.summarize_pmc
+
+    def gemm_totals(d, counter):
+        tot, disp = 0.0, {}
+        for name, did, v in _pmc_rows(d, counter):
+            if any(m in name for m in GEMM_KERNELS):
+                tot += v
+                disp[did] = name
+        return tot, sum(1 for n in disp.values() if "gemm_kernel" in n)
+
+    def copy_kib(d, counter):
+        vals = {}
+        for name, did, v in _pmc_rows(d, counter):
+            if "copy" in name.lower() or "elementwise" in name.lower():
+                vals[did] = vals.get(did, 0.0) + v
+        if not vals:
+            raise SystemExit(f"no copy kernel dispatch in {d}")
+        return max(vals.values())
+
+    copy_bytes = args.copy_bytes
+    cf, cw = copy_kib(cfdir, "FETCH_SIZE"), copy_kib(cwdir, "WRITE_SIZE")
+    f_fetch, f_write = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    fetch, nf = gemm_totals(fdir, "FETCH_SIZE")
+    write, nw = gemm_totals(wdir, "WRITE_SIZE")
+    hbm = fetch * 1024.0 * f_fetch / nf + write * 1024.0 * f_write / nw
+    lines = [
+        "# HBM traffic of the NVFP4 GEMM entry points (gemm_kernel + lora_down_kernel),",
+        "# from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs, each scaled by the value",
+        "# the same counter reads for a plain device copy of known size.",
+        f"command: {args.pmc_command}",
+        f"gemm_source_sha256: {gemm_source_sha()}",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_scale: {f_fetch:.4f}",
+        f"write_scale: {f_write:.4f}",
+        f"gemm_launches: {nf}",
+        f"gemm_fetch_kib_total: {fetch:.1f}",
+        f"gemm_write_kib_total: {write:.1f}",
+        f"hbm_bytes_per_gemm_launch: {hbm:.1f}",
+    ]
+    text = "\n".join(lines) + "\n"
+    if args.pmc_out:
+        with open(args.pmc_out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the data flow is row-parallel and this build "
-              "runs on a single MI355X (the sharding plan is described in DESIGN.md).",
+        print("bench.py measures one GPU only: every step of the data flow is row-parallel, "
+              "and this build runs on a single MI355X (the sharding plan is in DESIGN.md).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from nvfp4_gemm_amd import synth
-    shape = synth.LAYERS[args.config]
-    layer = Layer(shape, args.seed)
+    if args.config == "single_linear":
+        work = Linear(args.seed)
+    else:
+        shape = synth.LAYERS[args.config]
+        work = Stack(shape, args.seed, shape.layers)
     st = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    e0, e1 = ev(), ev()
-    e0.record(st)
-    layer.build_layouts()
-    e1.record(st)
-    torch.cuda.synchronize()
-    layout_ms = e0.elapsed_time(e1)
-    calls = layer.calls()
+    calls = work.calls()
+    torch.cuda.reset_peak_memory_stats()
     for _ in range(args.warmup):
         for c in calls:
             c[3]()
@@ -238,6 +503,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+    peak_hbm = torch.cuda.max_memory_allocated()
     per_kind = {}
     for s in range(args.steps):
         for (a, b), c in zip(evs[s], calls):
@@ -266,7 +532,7 @@ def main():
             d["GB/s"] = gbs
             d["hbm_frac"] = gbs / PEAK_HBM_GBS
         kinds[kind] = d
-    pact_stash, bf16_stash = layer.stash_bytes()
+    cfg = work.config()
     out = {
         "metric": METRIC,
         "value": value,
@@ -280,26 +546,31 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": shape.name, "tokens": shape.tokens, "hidden": shape.hidden,
-                   "intermediate": shape.inter, "kv": shape.kv, "lora_rank": shape.rank,
-                   "lora_scale": shape.lora_scale, "step": "layer forward + input-gradient backward, "
-                   "7 frozen NVFP4 projections, fused RMSNorm/SiLU quantizers"},
-        "tokens_per_s": shape.tokens / (ms_step * 1e-3),
+        "config": cfg,
+        "tokens_per_s": work.M / (ms_step * 1e-3),
         "frozen_gemm_tflops_kernel_time": gemm["flops"] / (gemm["ms"] * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_F16_MFMA_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_F16_MFMA_TFLOPS,
+                     "traffic": traffic_summary(cfg["workload"]),
                      "kernel": "NVFP4 GEMM entry points (fwd + dgrad: LoRA-down + main GEMM kernels), "
                                "frozen + LoRA FLOPs per launch / mean launch time",
+                     "traffic_unit": "HBM bytes per GEMM launch",
                      "fp4_peak_context": PEAK_FP4_TFLOPS},
         "kernels": kinds,
-        "stash_bytes": {"pact_nvfp4": pact_stash, "bf16_lora": bf16_stash,
-                        "ratio": bf16_stash / pact_stash},
-        "layout_build_ms_7_projections": layout_ms,
-        "peak_hbm_bytes": torch.cuda.max_memory_allocated(),
+        "layout_build_ms": work.layout_ms,
+        "peak_hbm_bytes": peak_hbm,
     }
+    sb = work.stash_bytes()
+    if sb:
+        out["stash_bytes"] = {"pact_nvfp4": sb[0], "bf16_lora": sb[1], "ratio": sb[1] / sb[0]}
+    if not args.no_isolated:
+        out["kernels_isolated_cache_flushed"] = isolated_timing(torch, calls)
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or min(shape.tokens, 256)
-        out["cpu_baseline"] = cpu_baseline(shape, layer.li, n)
+        if args.config == "single_linear":
+            out["cpu_baseline"] = cpu_baseline_linear(work)
+        else:
+            n = args.cpu_sample_tokens or min(work.M, 1024)
+            out["cpu_baseline"] = cpu_baseline_layer(work.S, work.li0, n)
     print(json.dumps(out), flush=True)
 
 

@@ -155,9 +155,8 @@ struct GemmShape {
     static constexpr int N_SC_I = ROWS / 64;    // 256 B loads per stage: 64 rows x 4 B
     static constexpr int LPW = (N_CODE_I + N_SC_I) / G;  // loads per wavefront per stage
     static constexpr int NQC = N_CODE_I / G;              // of which code loads
-    // partial-tile exchange: WK == 2: 8 fragments per wavefront;
-    // WK == 4: 8 fragment slots per wavefront per round (2 rounds)
-    static constexpr int RED_BYTES = WK == 1 ? 0 : 4 * 8 * 4096;
+    // partial-tile exchange: 4 fragments (one column) per wavefront per round
+    static constexpr int RED_BYTES = WK == 1 ? 0 : 4 * 4 * 4096;
     static constexpr int LDS_BYTES = WK * GROUP_BYTES > RED_BYTES ? WK * GROUP_BYTES : RED_BYTES;
     static_assert(G * WK == 4, "four wavefronts");
     static_assert(N_CODE_I % G == 0 && N_SC_I % G == 0, "loads split evenly");
@@ -474,75 +473,32 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
             for (int fn = 0; fn < 4; ++fn) store_frag(acc[fm][fn], mw + 32 * fm, nw + 32 * fn);
-    } else if constexpr (WK == 2) {
-        // group 0 keeps fragment rows 0-1, group 1 rows 2-3; each wavefront
-        // hands the other half to its partner (same position, other group).
-        // Sum order: group 0's partial + group 1's partial.
-        lds_barrier();
-        uint8_t *const mine = lds + wave * 8 * 4096;
-        const uint8_t *const other = lds + ((1 - grp) * G + wi) * 8 * 4096;
-        auto exchange = [&](auto Kc) {
-            constexpr int KEEP = decltype(Kc)::value;  // first kept fragment row
-            constexpr int GIVE = 2 - KEEP;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int fn = 0; fn < 4; ++fn) put_frag(mine + (i * 4 + fn) * 4096, acc[GIVE + i][fn]);
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int fn = 0; fn < 4; ++fn) {
-                    const float16_t o = get_frag(other + (i * 4 + fn) * 4096);
-                    float16_t &a = acc[KEEP + i][fn];
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) a[e] = KEEP == 0 ? a[e] + o[e] : o[e] + a[e];
-                    store_frag(a, mw + 32 * (KEEP + i), nw + 32 * fn);
-                }
-        };
-        if (grp == 0)
-            exchange(std::integral_constant<int, 0>());
-        else
-            exchange(std::integral_constant<int, 2>());
     } else {
-        // WK == 4: wavefront w keeps fragment row w.  Two rounds of two
-        // fragment columns; slot (q, fm, fn') of wavefront q at
-        // lds + ((q * 4 + fm) * 2 + fn') * 4 KB.  Sum order: wavefront 0, 1, 2, 3.
-        auto round = [&](auto Wc, int rnd) {
-            constexpr int W = decltype(Wc)::value;
+        // Partial tiles summed through LDS, one fragment column per round:
+        // every wavefront writes its 4 fragments of the column to slot
+        // (wave, fm); the owner of a fragment row then reads the WK partials
+        // of it (its own included) and adds them in K-range order.  Fragment
+        // row fm belongs to the wavefront of K range fm / (4 / WK) at the same
+        // position in its group.
+        constexpr int ROWS_PER_OWNER = 4 / WK;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
             lds_barrier();
 #pragma unroll
-            for (int fm = 0; fm < 4; ++fm)
-                if (fm != W)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        put_frag(lds + ((W * 4 + fm) * 2 + j) * 4096, acc[fm][2 * rnd + j]);
+            for (int fm = 0; fm < 4; ++fm) put_frag(lds + (wave * 4 + fm) * 4096, acc[fm][c]);
             lds_barrier();
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float16_t sum;
+            for (int i = 0; i < ROWS_PER_OWNER; ++i) {
+                const int fm = grp * ROWS_PER_OWNER + i;
+                float16_t sum = get_frag(lds + ((0 * G + wi) * 4 + fm) * 4096);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float16_t part = q == W ? acc[W][2 * rnd + j] : get_frag(lds + ((q * 4 + W) * 2 + j) * 4096);
-                    if (q == 0)
-                        sum = part;
-                    else
+                for (int q = 1; q < WK; ++q) {
+                    const float16_t part = get_frag(lds + ((q * G + wi) * 4 + fm) * 4096);
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) sum[e] = sum[e] + part[e];
+                    for (int e = 0; e < 16; ++e) sum[e] = sum[e] + part[e];
                 }
-                store_frag(sum, mw + 32 * W, nw + 32 * (2 * rnd + j));
+                store_frag(sum, mw + 32 * fm, nw + 32 * c);
             }
-        };
-#pragma unroll
-        for (int rnd = 0; rnd < 2; ++rnd) {
-            if (wave == 0)
-                round(std::integral_constant<int, 0>(), rnd);
-            else if (wave == 1)
-                round(std::integral_constant<int, 1>(), rnd);
-            else if (wave == 2)
-                round(std::integral_constant<int, 2>(), rnd);
-            else
-                round(std::integral_constant<int, 3>(), rnd);
         }
     }
 }
