@@ -23,7 +23,12 @@ cached NVFP4 layouts are built once before timing.
 
 Prints ONE JSON line.  `value` = frozen-projection GEMM FLOPs of the step
 (2 M N K over every forward and input-gradient GEMM) / wall time of the whole
-step (every kernel included), in TFLOP/s.
+step (every kernel included), in TFLOP/s.  The step is captured once as a HIP
+graph and the timed region replays it (a training loop launches the same
+step every iteration; the graph removes the per-call host overhead of the
+Python binding).  A second timed region runs the step eagerly with events
+around every call on its stream: the per-kernel durations and the roofline
+figures come from it.
 
 Other modes (used to calibrate and summarize rocprofv3 counter runs):
   --copy-calibration MIB   runs a plain device-to-device copy of MIB MiB
@@ -64,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: the whole batch, at most 1024)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step without graph capture")
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the cache-flushed timing of the memory-bound kernels")
     ap.add_argument("--seed", type=int, default=0)
@@ -501,8 +508,33 @@ def main():
             b.record(st)
     t_end.record(st)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    eager_ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = eager_ms_step
+    timing = "eager"
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            for c in calls:
+                c[3]()
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c[3]()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev(), ev()
+        g0.record(st)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(st)
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / args.steps
+        timing = "hip_graph_replay"
+        del graph
     peak_hbm = torch.cuda.max_memory_allocated()
     per_kind = {}
     for s in range(args.steps):
@@ -541,6 +573,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_timing": timing,
+        "eager_ms_per_step": eager_ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -105,6 +105,71 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gsize;
 }
 
+// Epilogue of one 32x32 accumulator fragment whose rows start at mb and
+// columns at nb: y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s.Q^T
+// (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by one BF16
+// MFMA per 16 ranks, then C is added and y rounded to BF16 and stored.
+__device__ __forceinline__ void store_frag(const GemmArgs &p, float16_t &a, int mb, int nb, int lane) {
+    const int h = lane >> 5, lr = lane & 31;
+    const int n = nb + lr;
+    const float dw = n < p.N ? p.b_d[n] : 0.0f;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        const int m = mb + 8 * e4 + 4 * h;
+        float dx[4];
+        if (m + 3 < p.M) {
+            const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
+            dx[0] = v[0];
+            dx[1] = v[1];
+            dx[2] = v[2];
+            dx[3] = v[3];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dx[q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float y = a[4 * e4 + q] * dx[q];
+            a[4 * e4 + q] = y * dw;
+        }
+    }
+    if (p.T) {
+        const int mr = min(mb + lr, p.M - 1);
+        const int nr = min(n, p.N - 1);
+        for (int kk = 0; kk < p.rpad; kk += 16) {
+            const u32x4 va = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + kk + 8 * h);
+            u32x4 vb;
+            const int j0 = kk + 8 * h;
+            if (p.q_sj == 1 && (p.r & 7) == 0) {
+                vb = u32x4{0u, 0u, 0u, 0u};
+                if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ja = j0 + 2 * e, jb = ja + 1;
+                    const uint32_t lo = ja < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)ja * p.q_sj] : 0u;
+                    const uint32_t hi = jb < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)jb * p.q_sj] : 0u;
+                    w[e] = lo | (hi << 16);
+                }
+                vb = u32x4{w[0], w[1], w[2], w[3]};
+            }
+            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                        __builtin_bit_cast(bf16x8_t, vb), a, 0, 0, 0);
+        }
+    }
+    if (n >= p.N) return;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m >= p.M) continue;
+        float y = a[e];
+        const int64_t off = (int64_t)m * p.ldy + n;
+        if (p.C) y = y + bf16_to_f32(p.C[off]);
+        p.Y[off] = (uint16_t)f32_to_bf16_bits(y);
+    }
+}
+
 // Main kernel.  Every wavefront owns a 128 x 128 accumulator tile (4 x 4
 // fragments of 32 x 32, 256 FP32 per lane) and decodes its own MFMA operands
 // from the packed NVFP4 stage in LDS: per K16 step it converts 8 fragments
@@ -383,68 +448,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     wait_global_loads();
 
     // ---- epilogue: row scales, LoRA term, residual, BF16 store ----
-    // y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s . Q^T
-    // (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by
-    // one BF16 MFMA per 16 ranks, then C is added and y rounded.
-    auto store_frag = [&](float16_t &a, int mb, int nb) {
-        const int n = nb + lr;
-        const float dw = n < p.N ? p.b_d[n] : 0.0f;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int m = mb + 8 * e4 + 4 * h;
-            float dx[4];
-            if (m + 3 < p.M) {
-                const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
-                dx[0] = v[0];
-                dx[1] = v[1];
-                dx[2] = v[2];
-                dx[3] = v[3];
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) dx[q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float y = a[4 * e4 + q] * dx[q];
-                a[4 * e4 + q] = y * dw;
-            }
-        }
-        if (p.T) {
-            const int mr = min(mb + lr, p.M - 1);
-            const int nr = min(n, p.N - 1);
-            for (int kk = 0; kk < p.rpad; kk += 16) {
-                const u32x4 va = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + kk + 8 * h);
-                u32x4 vb;
-                const int j0 = kk + 8 * h;
-                if (p.q_sj == 1 && (p.r & 7) == 0) {
-                    vb = u32x4{0u, 0u, 0u, 0u};
-                    if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
-                } else {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int ja = j0 + 2 * e, jb = ja + 1;
-                        const uint32_t lo = ja < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)ja * p.q_sj] : 0u;
-                        const uint32_t hi = jb < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)jb * p.q_sj] : 0u;
-                        w[e] = lo | (hi << 16);
-                    }
-                    vb = u32x4{w[0], w[1], w[2], w[3]};
-                }
-                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
-                                                            __builtin_bit_cast(bf16x8_t, vb), a, 0, 0, 0);
-            }
-        }
-        if (n >= p.N) return;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (m >= p.M) continue;
-            float y = a[e];
-            const int64_t off = (int64_t)m * p.ldy + n;
-            if (p.C) y = y + bf16_to_f32(p.C[off]);
-            p.Y[off] = (uint16_t)f32_to_bf16_bits(y);
-        }
-    };
     const int mw = m0 + a_row0, nw = n0 + wn * 128;
 
     // partial fragment slot: [e4][lane][4 floats], 4 KB, conflict-free
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn) store_frag(acc[fm][fn], mw + 32 * fm, nw + 32 * fn);
+            for (int fn = 0; fn < 4; ++fn) store_frag(p, acc[fm][fn], mw + 32 * fm, nw + 32 * fn, lane);
     } else {
         // Partial tiles summed through LDS, one fragment column per round:
         // every wavefront writes its 4 fragments of the column to slot
@@ -497,10 +500,218 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) sum[e] = sum[e] + part[e];
                 }
-                store_frag(sum, mw + 32 * fm, nw + 32 * c);
+                store_frag(p, sum, mw + 32 * fm, nw + 32 * c, lane);
             }
         }
     }
+}
+
+// ---- 256 x 256 kernel with one decode per workgroup --------------------------
+// For output tiles of 256 x 256 (enough of them to fill the GPU).  Eight
+// wavefronts (two per SIMD) each own 128 x 64 of the tile (4 x 2 fragments).
+// Each K32 phase is decoded once per workgroup: thread t converts row t of the
+// tile (rows 0-255 of A, 256-511 of B) into FP16 in an LDS tile laid out in
+// MFMA fragment order, so the VALU cost is 2 operations per MFMA instead of
+// the 6 a per-wavefront decode of a 128 x 64 tile would take.
+//
+// LDS: the packed stage ring of the main kernel (4 buffers of 64 K-elements,
+// rows of 32 code bytes with halves swapped on rows with bit 3 set, then the
+// rows' 4 scale bytes) and two FP16 phase tiles of 32 KB:
+//   F[g][s][lane] 16 bytes, g = 32-row group (0-7 A, 8-15 B), s = K16 step,
+//   lane (r, h) = row r of the group, K [16 s + 8 h, 16 s + 8 h + 8).
+// Phase p (one barrier, mid-phase):
+//   first half:  MFMAs of step 0 (fragments read before), the decode of
+//                phase p+1 into F[(p+1) & 1] from packed codes read one phase
+//                earlier, the reads of this phase's step-1 fragments; on even
+//                p the loads of stage p/2 + 3 are issued and each wavefront
+//                waits for stage p/2 + 1;
+//   barrier:     F[(p+1) & 1] complete; everyone is past phase p-1's reads;
+//   second half: MFMAs of step 1, reads of phase p+1's step-0 fragments and
+//                of phase p+2's packed codes.
+struct Gemm8Shape {
+    static constexpr int BM = 256, BN = 256, ROWS = 512;
+    static constexpr int PCODE = ROWS * 32;
+    static constexpr int STAGE = ROWS * 36;           // 18 KB
+    static constexpr int RING = kNBuf * STAGE;        // 72 KB
+    static constexpr int FPH = ROWS * 32 * 2;         // 32 KB FP16 phase tile
+    static constexpr int LDS_BYTES = RING + 2 * FPH;  // 136 KB
+    static constexpr int LPW = 3;                     // stage loads per wavefront: 2 code, 1 scale
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
+    using SH = Gemm8Shape;
+    constexpr int STAGE = SH::STAGE, PCODE = SH::PCODE, FPH = SH::FPH, LPW = SH::LPW;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
+    uint8_t *const ring = lds;
+    uint8_t *const F0 = lds + SH::RING;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 wavefronts of 128 x 64
+    const int tiles_m = (p.M + SH::BM - 1) / SH::BM;
+    const int tiles_n = (p.N + SH::BN - 1) / SH::BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * SH::BM, n0 = tn * SH::BN;
+    const int K = p.K;
+    const int nblk = K >> 4;
+    const int S = K / kSK;  // stages (K % 64 == 0 for this kernel)
+
+    // ---- stage loads: wavefront w issues code loads w (A rows 32w..) and
+    // w + 8 (B rows), and scale load w (rows 64w.., A when w < 4) ----
+    const __amdgpu_buffer_rsrc_t rs_ac =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.a_codes, (short)0, (int)(p.a_bytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_bc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.b_codes, (short)0, (int)(p.b_bytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_sc = wave < 4
+        ? __builtin_amdgcn_make_buffer_rsrc((void *)p.a_scales, (short)0, (int)(p.a_bytes >> 3), kRsrcWord3)
+        : __builtin_amdgcn_make_buffer_rsrc((void *)p.b_scales, (short)0, (int)(p.b_bytes >> 3), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_none =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.a_codes, (short)0, 0, kRsrcWord3);
+    const int gp = (lane & 1) ^ ((lane >> 4) & 1);
+    uint32_t off_a, off_b, off_s;
+    {
+        const int ra = 32 * wave + (lane >> 1);                 // A tile row
+        const int rb = 32 * wave + (lane >> 1);                 // B tile row (code load w + 8)
+        off_a = (uint32_t)min(m0 + ra, p.M - 1) * (uint32_t)(K >> 1) + 16u * (uint32_t)gp;
+        off_b = (uint32_t)min(n0 + rb, p.N - 1) * (uint32_t)(K >> 1) + 16u * (uint32_t)gp;
+        const int rs = 64 * wave + lane;                        // tile row of the scale load
+        const int crow = rs < SH::BM ? min(m0 + rs, p.M - 1) : min(n0 + rs - SH::BM, p.N - 1);
+        off_s = (uint32_t)crow * (uint32_t)nblk;
+    }
+    auto issue_stage = [&](int s) {
+        uint8_t *const buf = ring + (s % kNBuf) * STAGE;
+        const bool live = s < S;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_ac : rs_none, (lds_void_t *)(buf + wave * 1024), 16,
+                                                 (int)off_a, s * (kSK / 2), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_bc : rs_none, (lds_void_t *)(buf + (wave + 8) * 1024),
+                                                 16, (int)off_b, s * (kSK / 2), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_sc : rs_none, (lds_void_t *)(buf + PCODE + wave * 256), 4,
+                                                 (int)off_s, s * (kSK / 16), 0, 0);
+    };
+
+    // ---- decode: thread t owns tile row t; phase q = half (q & 1) of stage q/2 ----
+    const int drow = tid;
+    const int dg = drow >> 5, dlr = drow & 31;
+    const int rd_packed = drow * 32;
+    const int rd_sc = PCODE + drow * 4;
+    const int sw = (drow >> 3) & 1;
+    uint8_t *const fwr = F0 + ((dg * 2) * 64 + dlr) * 16;  // + step * 1024 + h * 512
+    u32x4 pw;        // packed codes of the next phase to decode
+    uint32_t psc;    // its two block-scale bytes
+    auto read_packed = [&](int q) {
+        const uint8_t *buf = ring + ((q >> 1) % kNBuf) * STAGE;
+        const int pc = q & 1;
+        pw = *reinterpret_cast<const u32x4 *>(buf + rd_packed + 16 * (pc ^ sw));
+        psc = *reinterpret_cast<const uint16_t *>(buf + rd_sc + 2 * pc);
+    };
+    auto decode_phase = [&](int q) {
+        const half2_t sh = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(psc, 1.0f, false);
+        half2_t s0, s1;
+        s0[0] = sh[0];
+        s0[1] = sh[0];
+        s1[0] = sh[1];
+        s1[1] = sh[1];
+        uint8_t *const fb = fwr + (q & 1) * FPH;
+        *reinterpret_cast<half8_t *>(fb) = decode8(pw.x, s0);          // step 0, h 0
+        *reinterpret_cast<half8_t *>(fb + 512) = decode8(pw.y, s0);    // step 0, h 1
+        *reinterpret_cast<half8_t *>(fb + 1024) = decode8(pw.z, s1);   // step 1, h 0
+        *reinterpret_cast<half8_t *>(fb + 1536) = decode8(pw.w, s1);   // step 1, h 1
+    };
+
+    // ---- fragment reads: A groups 4 wm + fm, B groups 8 + 2 wn + fn ----
+    auto read_frags = [&](int q, int st, half8_t (&fr)[6]) {
+        const uint8_t *fb = F0 + (q & 1) * FPH + (st * 64 + lane) * 16;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            fr[f] = *reinterpret_cast<const half8_t *>(fb + ((4 * wm + f) * 2) * 1024);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+            fr[4 + f] = *reinterpret_cast<const half8_t *>(fb + ((8 + 2 * wn + f) * 2) * 1024);
+    };
+
+    float16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto mfma_step = [&](const half8_t (&fr)[6]) {
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 2; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[fm], fr[4 + fn], acc[fm][fn], 0, 0, 0);
+    };
+
+    half8_t f0[6], f1[6];
+    const int nph = 2 * S;
+    if (S > 0) {
+        issue_stage(0);
+        issue_stage(1);
+        issue_stage(2);
+        wait_vmcnt_lds_barrier<2 * LPW>();  // stage 0 of every wavefront
+        read_packed(0);
+        decode_phase(0);
+        read_packed(1);
+        lds_barrier();
+        read_frags(0, 0, f0);
+    }
+    // Phase q.  The barrier is a hard scheduling boundary (sched_barrier), so
+    // the two halves keep their own MFMAs.
+    auto phase = [&](auto Ec, int q) {
+        constexpr bool EVEN = decltype(Ec)::value;
+        // first half: step-0 MFMAs, step-1 fragment reads, decode of phase q+1
+        if (EVEN) issue_stage((q >> 1) + 3);
+        read_frags(q, 1, f1);
+        decode_phase(q + 1);
+        mfma_step(f0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+            if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            if (i >= 2 && i < 6) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // 1 LDS write
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // stage q/2 + 1 (read from the next phase on) has landed: stages
+        // q/2 + 1 .. q/2 + 3 were in flight
+        if (EVEN)
+            wait_vmcnt_lds_barrier<2 * LPW>();
+        else
+            lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // second half: step-1 MFMAs, step-0 fragments of phase q+1, packed
+        // codes of phase q+2
+        read_frags(q + 1, 0, f0);
+        read_packed(q + 2);
+        mfma_step(f1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int q = 0; q < nph; q += 2) {
+        phase(std::integral_constant<bool, true>(), q);
+        phase(std::integral_constant<bool, false>(), q + 1);
+    }
+    wait_global_loads();
+
+    const int mw = m0 + 128 * wm, nw = n0 + 64 * wn;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) store_frag(p, acc[fm][fn], mw + 32 * fm, nw + 32 * fn, lane);
 }
 
 // ---- LoRA down-projection --------------------------------------------------
@@ -616,7 +827,14 @@ static pact_status run_gemm(const GemmArgs &a, hipStream_t st) {
         }
     }
     switch (best) {
-        case 0: launch_gemm_cfg<2, 2, 1>(a, st); break;
+        case 0:
+            if (a.K % kSK == 0) {
+                const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+                hipLaunchKernelGGL(gemm8_kernel, dim3(tiles), dim3(512), 0, st, a);
+            } else {
+                launch_gemm_cfg<2, 2, 1>(a, st);
+            }
+            break;
         case 1: launch_gemm_cfg<2, 1, 2>(a, st); break;
         case 2: launch_gemm_cfg<1, 2, 2>(a, st); break;
         default: launch_gemm_cfg<1, 1, 4>(a, st); break;

@@ -96,7 +96,8 @@ def test_single_linear_workload_full():
 
 @pytest.mark.parametrize("M,N,K,r", [(1024, 2048, 2048, 16), (1024, 8192, 2048, 16),
                                      (2048, 3072, 8192, 32), (4096, 256, 1536, 16),
-                                     (2048, 6144, 512, 16), (2304, 6160, 528, 8)])
+                                     (2048, 6144, 512, 16), (2304, 6160, 528, 8),
+                                     (4096, 2048, 4096, 16), (4500, 4208, 576, 8)])
 def test_gemm_layer_sizes_sampled_rows(M, N, K, r):
     """Projection shapes of the layer workloads in the kernel's real launch
     configuration; the oracle checks a sample of rows (first, last, strided)."""
