@@ -29,6 +29,7 @@
 // LoRA-up product T Q^T is accumulated by BF16 MFMAs into the row-scaled
 // accumulators in the epilogue.
 #include <type_traits>
+#include <utility>
 
 #include "pact_device.h"
 #include "pact_host.h"
@@ -105,35 +106,83 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gsize;
 }
 
-// Epilogue of one 32x32 accumulator fragment whose rows start at mb and
-// columns at nb: y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s.Q^T
-// (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by one BF16
-// MFMA per 16 ranks, then C is added and y rounded to BF16 and stored.
-__device__ __forceinline__ void store_frag(const GemmArgs &p, float16_t &a, int mb, int nb, int lane) {
+// Epilogue of a 32x32 accumulator fragment whose rows start at mb and columns
+// at nb: y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s.Q^T
+// (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by one
+// BF16 MFMA per 16 ranks, then C is added and y rounded to BF16 and stored.
+// Split in two so that callers issue the loads of several fragments before
+// finishing any of them (the epilogue is otherwise bound by one global-load
+// latency per fragment).
+struct EpiIn {
+    float dx[16];    // d_a of the lane's 16 rows
+    float dw;        // d_b of the lane's column
+    u32x4 t[2], q[2];  // LoRA operands, ranks [0, 32) (prefetched when rpad <= 32)
+    uint32_t c[8];   // C of the lane's 16 elements, BF16 pairs
+};
+
+__device__ __forceinline__ bool epi_lora_prefetch(const GemmArgs &p) {
+    return p.T && p.rpad <= 32 && p.q_sj == 1 && (p.r & 7) == 0;
+}
+
+__device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int lane, EpiIn &in) {
     const int h = lane >> 5, lr = lane & 31;
     const int n = nb + lr;
-    const float dw = n < p.N ? p.b_d[n] : 0.0f;
+    in.dw = n < p.N ? p.b_d[n] : 0.0f;
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
         const int m = mb + 8 * e4 + 4 * h;
-        float dx[4];
         if (m + 3 < p.M) {
             const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
-            dx[0] = v[0];
-            dx[1] = v[1];
-            dx[2] = v[2];
-            dx[3] = v[3];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) in.dx[4 * e4 + q] = v[q];
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dx[q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float y = a[4 * e4 + q] * dx[q];
-            a[4 * e4 + q] = y * dw;
+            for (int q = 0; q < 4; ++q) in.dx[4 * e4 + q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
         }
     }
-    if (p.T) {
+    if (epi_lora_prefetch(p)) {
+        const int mr = min(mb + lr, p.M - 1);
+        const int nr = min(n, p.N - 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j0 = 16 * i + 8 * h;
+            in.t[i] = u32x4{0u, 0u, 0u, 0u};
+            in.q[i] = u32x4{0u, 0u, 0u, 0u};
+            if (16 * i < p.rpad) in.t[i] = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + j0);
+            if (j0 < p.r) in.q[i] = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
+        }
+    }
+    if (p.C) {
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = 2 * e2 + i;
+                const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < p.M && n < p.N) w |= (uint32_t)p.C[(int64_t)m * p.ldy + n] << (16 * i);
+            }
+            in.c[e2] = w;
+        }
+    }
+}
+
+__device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int mb, int nb, int lane,
+                                           const EpiIn &in) {
+    const int h = lane >> 5, lr = lane & 31;
+    const int n = nb + lr;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float y = a[e] * in.dx[e];
+        a[e] = y * in.dw;
+    }
+    if (epi_lora_prefetch(p)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            if (16 * i < p.rpad)
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, in.t[i]),
+                                                            __builtin_bit_cast(bf16x8_t, in.q[i]), a, 0, 0, 0);
+    } else if (p.T) {
         const int mr = min(mb + lr, p.M - 1);
         const int nr = min(n, p.N - 1);
         for (int kk = 0; kk < p.rpad; kk += 16) {
@@ -164,10 +213,41 @@ __device__ __forceinline__ void store_frag(const GemmArgs &p, float16_t &a, int 
         const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m >= p.M) continue;
         float y = a[e];
-        const int64_t off = (int64_t)m * p.ldy + n;
-        if (p.C) y = y + bf16_to_f32(p.C[off]);
-        p.Y[off] = (uint16_t)f32_to_bf16_bits(y);
+        if (p.C) y = y + bf16_to_f32((uint16_t)(in.c[e >> 1] >> (16 * (e & 1))));
+        p.Y[(int64_t)m * p.ldy + n] = (uint16_t)f32_to_bf16_bits(y);
     }
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (indices known at
+// compile time, so register arrays indexed by them stay in registers).
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Epilogue of F fragments in groups of G: the loads of a group are issued
+// together, then the group is finished.  accf(I) returns fragment I; mb[I],
+// nb[I] its first row and column.
+template <int F, int G, typename AccFn>
+__device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
+                                          const int (&nb)[F]) {
+    static_assert(F % G == 0, "whole groups");
+    static_for<F / G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value * G;
+        EpiIn in[G];
+        static_for<G>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            epi_load(p, mb[g + i], nb[g + i], lane, in[i]);
+        });
+        static_for<G>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            epi_finish(p, accf(std::integral_constant<int, g + i>{}), mb[g + i], nb[g + i], lane, in[i]);
+        });
+    });
 }
 
 // Main kernel.  Every wavefront owns a 128 x 128 accumulator tile (4 x 4
@@ -472,10 +552,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     };
 
     if constexpr (WK == 1) {
+        int mbs[16], nbs[16];
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < 4; ++fn) store_frag(p, acc[fm][fn], mw + 32 * fm, nw + 32 * fn, lane);
+        for (int i = 0; i < 16; ++i) {
+            mbs[i] = mw + 32 * (i >> 2);
+            nbs[i] = nw + 32 * (i & 3);
+        }
+        epi_frags<16, 4>(p, lane, [&](auto ic) -> float16_t & {
+            constexpr int i = decltype(ic)::value;
+            return acc[i >> 2][i & 3];
+        }, mbs, nbs);
     } else {
         // Partial tiles summed through LDS, one fragment column per round:
         // every wavefront writes its 4 fragments of the column to slot
@@ -484,6 +570,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         // row fm belongs to the wavefront of K range fm / (4 / WK) at the same
         // position in its group.
         constexpr int ROWS_PER_OWNER = 4 / WK;
+        float16_t own[ROWS_PER_OWNER][4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             lds_barrier();
@@ -500,9 +587,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) sum[e] = sum[e] + part[e];
                 }
-                store_frag(p, sum, mw + 32 * fm, nw + 32 * c, lane);
+                own[i][c] = sum;
             }
         }
+        constexpr int NF = 4 * ROWS_PER_OWNER;
+        int mbs[NF], nbs[NF];
+#pragma unroll
+        for (int i = 0; i < ROWS_PER_OWNER; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                mbs[4 * i + c] = mw + 32 * (grp * ROWS_PER_OWNER + i);
+                nbs[4 * i + c] = nw + 32 * c;
+            }
+        epi_frags<NF, 4>(p, lane, [&](auto ic) -> float16_t & {
+            constexpr int i = decltype(ic)::value;
+            return own[i >> 2][i & 3];
+        }, mbs, nbs);
     }
 }
 
@@ -708,10 +808,16 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     wait_global_loads();
 
     const int mw = m0 + 128 * wm, nw = n0 + 64 * wn;
+    int mbs[8], nbs[8];
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn) store_frag(p, acc[fm][fn], mw + 32 * fm, nw + 32 * fn, lane);
+    for (int i = 0; i < 8; ++i) {
+        mbs[i] = mw + 32 * (i >> 1);
+        nbs[i] = nw + 32 * (i & 1);
+    }
+    epi_frags<8, 2>(p, lane, [&](auto ic) -> float16_t & {
+        constexpr int i = decltype(ic)::value;
+        return acc[i >> 1][i & 1];
+    }, mbs, nbs);
 }
 
 // ---- LoRA down-projection --------------------------------------------------
@@ -723,6 +829,7 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
 // One workgroup of 16 wavefronts per 16 rows: each wavefront takes a slice of
 // K, and the 16 partial tiles are summed through LDS in a fixed order.
 constexpr int kDownWaves = 16;
+constexpr int kDownU = 8;
 
 __global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int64_t ldx, int M, int Kl,
                                                          const uint16_t *Ps, int64_t p_sj, int64_t p_sk,
@@ -738,26 +845,35 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int6
     for (int f = 0; f < rpad / 16; ++f) {
         const int j = 16 * f + (lane & 15);
         float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k0 = kb; k0 < ke; k0 += 32) {
-            const int k = k0 + kg;
-            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-            if (k < ke) {
-                va = *reinterpret_cast<const u32x4 *>(X + (int64_t)row * ldx + k);
-                if (j < r) {
-                    if (p_sk == 1) {
-                        vb = *reinterpret_cast<const u32x4 *>(Ps + (int64_t)j * p_sj + k);
-                    } else {
-                        uint32_t t[4];
+        // kDownU chunks of 32 K per iteration: all their loads are issued
+        // before the MFMAs, so the loop is not bound by one load latency per chunk
+        for (int k0 = kb; k0 < ke; k0 += 32 * kDownU) {
+            u32x4 va[kDownU], vb[kDownU];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            t[e] = (uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e) * p_sk] |
-                                   ((uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e + 1) * p_sk] << 16);
-                        vb = u32x4{t[0], t[1], t[2], t[3]};
+            for (int u = 0; u < kDownU; ++u) {
+                const int k = k0 + 32 * u + kg;
+                va[u] = u32x4{0u, 0u, 0u, 0u};
+                vb[u] = u32x4{0u, 0u, 0u, 0u};
+                if (k < ke) {
+                    va[u] = *reinterpret_cast<const u32x4 *>(X + (int64_t)row * ldx + k);
+                    if (j < r) {
+                        if (p_sk == 1) {
+                            vb[u] = *reinterpret_cast<const u32x4 *>(Ps + (int64_t)j * p_sj + k);
+                        } else {
+                            uint32_t t[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                t[e] = (uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e) * p_sk] |
+                                       ((uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e + 1) * p_sk] << 16);
+                            vb[u] = u32x4{t[0], t[1], t[2], t[3]};
+                        }
                     }
                 }
             }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va),
-                                                          __builtin_bit_cast(bf16x8_t, vb), acc, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < kDownU; ++u)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[u]),
+                                                              __builtin_bit_cast(bf16x8_t, vb[u]), acc, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[w][4 * (lane >> 4) + e][lane & 15] = acc[e];
