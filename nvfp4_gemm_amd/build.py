@@ -31,15 +31,29 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-I", BUILD, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
+def _sigmoid_table() -> None:
+    """Generates the SiLU kernel's sigma32 table (a host program run at build time)."""
+    exe = os.path.join(BUILD, "gen_sigmoid_table")
+    cmd = [os.environ.get("CXX", "g++"), "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+           os.path.join(CSRC, "gen_sigmoid_table.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"table generator build failed:\n{r.stderr}")
+    r = subprocess.run([exe, os.path.join(BUILD, "pact_sigmoid_table.inc")], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"table generator failed:\n{r.stderr}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _sigmoid_table()
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

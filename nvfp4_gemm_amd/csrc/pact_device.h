@@ -34,6 +34,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two FP32 values rounded to nearest-even BF16 (the hardware's packed
+// conversion), low half = a.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    const f2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, b2_t));
+}
+
 // E4M3 value of a scale byte (0x00..0x7E), exact, via the hardware decoder.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
     return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
@@ -108,19 +117,29 @@ __device__ __forceinline__ void encode_block16(const float v[16], float bamax, R
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             w[j >> 3] |= ((__float_as_uint(v[j]) >> 31) << 3) << (4 * (j & 7));
-    } else if (kBF16Exact) {
-        double rS = 1.0 / (double)S;
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-            float qa = quot_bf16(v[j], rS), qb = quot_bf16(v[j + 1], rS);
-            w[j >> 3] |= e2m1_encode2(qa, qb) << (4 * (j & 7));
-        }
     } else {
+        // quotients with the sign of x, then 4 converts per dword: the byte
+        // select of the converter places codes 2j, 2j+1 in byte j
+        float q[16];
+        if (kBF16Exact) {
+            const double rS = 1.0 / (double)S;
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-            float qa = quot_f32(v[j], S), qb = quot_f32(v[j + 1], S);
-            w[j >> 3] |= e2m1_encode2(qa, qb) << (4 * (j & 7));
+            for (int j = 0; j < 16; ++j) q[j] = quot_bf16(v[j], rS);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) q[j] = quot_f32(v[j], S);
         }
+        uint32_t a = 0u, b = 0u;
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[0], q[1], 1.0f, 0);
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[2], q[3], 1.0f, 1);
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[4], q[5], 1.0f, 2);
+        a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, q[6], q[7], 1.0f, 3);
+        b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[8], q[9], 1.0f, 0);
+        b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[10], q[11], 1.0f, 1);
+        b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[12], q[13], 1.0f, 2);
+        b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, q[14], q[15], 1.0f, 3);
+        w[0] = a;
+        w[1] = b;
     }
     codes_lo = w[0];
     codes_hi = w[1];

@@ -907,18 +907,6 @@ static void launch_gemm_cfg(const GemmArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, false>), dim3(tiles), dim3(256), 0, st, a);
 }
 
-static int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 // Wavefront arrangement: the estimated duration is the number of rounds of
 // one workgroup per CU times a wavefront's share of K, plus the partial-sum
 // exchange (about one stage for a 2-way K split, one and a half for 4-way).

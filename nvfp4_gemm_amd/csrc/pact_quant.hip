@@ -43,48 +43,18 @@ struct RowArgs {
     int cols;
 };
 
-// sigma32(g): correctly rounded binary32 value of g / (1 + exp(-g)) for BF16 g.
-// Outside 2^-25 <= |g| < 2^-6 the binary64 evaluation (error below 2^-51
-// relative) is far closer than any BF16 input's distance to a binary32
-// rounding midpoint (at least 2^-37 there), so one final rounding is exact.
-// Inside that range g/2 + g^2/4 can sit exactly on a midpoint and the true
-// value differs from it by about g^4/48, so the value is formed as the exact
-// binary64 sum hi = g/2 + g^2/4 plus the series tail
-// g^4 (-1/48 + g^2/480 - 17 g^4/80640 + 31 g^6/1451520), and an exact tie is
-// broken by the sign of the tail.
-__device__ __forceinline__ float next_up_f(float r) {
-    uint32_t b = __float_as_uint(r);
-    if (r >= 0.0f) return __uint_as_float(b + 1u);
-    return __uint_as_float(b - 1u);
-}
+// sigma32(g): the correctly rounded binary32 value of g / (1 + exp(-g)) for a
+// BF16 g, looked up in a table of all 65536 BF16 bit patterns (256 KB,
+// generated at build time by gen_sigmoid_table.cpp, which states the method).
+// The table is constant data of the code object; the library keeps no state.
+__device__ const uint32_t kSigmoidBits[65536] = {
+#include "pact_sigmoid_table.inc"
+};
 
-__device__ float sigmoid32(float gf) {
-    const float ag = fabsf(gf);
-    const double g = (double)gf;
-    if (ag >= 0x1p-25f && ag < 0x1p-6f) {
-        const double hi = 0.5 * g + 0.25 * (g * g);  // exact: span <= 41 bits
-        const double g2 = g * g;
-        const double corr =
-            (g2 * g2) * (-1.0 / 48.0 + g2 * (1.0 / 480.0 + g2 * (-17.0 / 80640.0 + g2 * (31.0 / 1451520.0))));
-        const double s = hi + corr;
-        float r = (float)s;
-        const double rd = (double)r;
-        if (rd != s) {
-            // neighbours lo < s < up of s in binary32
-            const float lo = rd < s ? r : -next_up_f(-r);
-            const float up = rd < s ? next_up_f(r) : r;
-            const double mid = 0.5 * ((double)lo + (double)up);  // exact
-            if (s == mid) {
-                const double delta = (hi - mid) + corr;  // hi - mid is exact
-                if (delta > 0.0) r = up;
-                else if (delta < 0.0) r = lo;
-            }
-        }
-        return r;
-    }
-    const double e = exp(-g);
-    return (float)(g / (1.0 + e));
-}
+__device__ __forceinline__ float sigmoid32_bits(uint32_t gbits) { return __uint_as_float(kSigmoidBits[gbits]); }
+
+// Workgroup barrier ordering LDS only.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int WPR>
 __device__ __forceinline__ void row_max3(float &a, float &b, float &c, float (*red)[4], int wave,
@@ -98,7 +68,7 @@ __device__ __forceinline__ void row_max3(float &a, float &b, float &c, float (*r
             red[wave][1] = b;
             red[wave][2] = c;
         }
-        __syncthreads();
+        lds_sync();
         const int w0 = lrow * WPR;
         a = red[w0][0];
         b = red[w0][1];
@@ -109,7 +79,7 @@ __device__ __forceinline__ void row_max3(float &a, float &b, float &c, float (*r
             b = fmaxf(b, red[w0 + w][1]);
             c = fmaxf(c, red[w0 + w][2]);
         }
-        __syncthreads();
+        lds_sync();
     }
 }
 
@@ -225,13 +195,13 @@ __global__ __launch_bounds__(256) void row_kernel(RowArgs a) {
                 redd[wave][0] = s;
                 redd[wave][1] = c;
             }
-            __syncthreads();
+            lds_sync();
             const int w0 = lrow * WPR;
             s = redd[w0][0];
             c = redd[w0][1];
 #pragma unroll
             for (int w = 1; w < WPR; ++w) dd_add_dd(s, c, redd[w0 + w][0], redd[w0 + w][1]);
-            __syncthreads();
+            lds_sync();
         }
         const double ss = s + c;
         const double ms = ss / (double)cols;
@@ -255,9 +225,7 @@ __global__ __launch_bounds__(256) void row_kernel(RowArgs a) {
             for (int j = 0; j < 8; ++j) {
                 const float t0 = v[2 * j] * r;
                 const float t1 = v[2 * j + 1] * r;
-                const uint32_t y0 = f32_to_bf16_bits(t0 * gv[2 * j]);
-                const uint32_t y1 = f32_to_bf16_bits(t1 * gv[2 * j + 1]);
-                xw[i][j] = y0 | (y1 << 16);  // y replaces x in registers
+                xw[i][j] = f32x2_to_bf16x2(t0 * gv[2 * j], t1 * gv[2 * j + 1]);  // y replaces x
             }
             if (a.y) store_block(a.y + row * a.ldy + 16 * b, xw[i]);
             unpack16(xw[i], v);
@@ -291,9 +259,9 @@ __global__ __launch_bounds__(256) void row_kernel(RowArgs a) {
             unpack16(uw[i], uv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float p0 = sigmoid32(gv[2 * j]) * uv[2 * j];
-                const float p1 = sigmoid32(gv[2 * j + 1]) * uv[2 * j + 1];
-                hw[i][j] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+                const float p0 = sigmoid32_bits(xw[i][j] & 0xFFFFu) * uv[2 * j];
+                const float p1 = sigmoid32_bits(xw[i][j] >> 16) * uv[2 * j + 1];
+                hw[i][j] = f32x2_to_bf16x2(p0, p1);
             }
             const int b = lt + T * i;
             if (a.y) store_block(a.y + row * a.ldy + 16 * b, hw[i]);
@@ -398,7 +366,7 @@ pact_status quantize_rows_launch(const uint16_t *x, int64_t ldx, int64_t rows, i
 // Exposes sigma32 for exhaustive verification.
 __global__ void sigmoid_probe_kernel(const uint16_t *g, float *out, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) out[i] = sigmoid32(bf16_to_f32(g[i]));
+    if (i < n) out[i] = sigmoid32_bits(g[i]);
 }
 
 }  // namespace pact
