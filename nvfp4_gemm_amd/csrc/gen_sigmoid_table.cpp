@@ -12,7 +12,18 @@
 // g^4 (-1/48 + g^2/480 - 17 g^4/80640 + 31 g^6/1451520), and an exact tie is
 // broken by the sign of the tail.
 //
-// Usage: gen_sigmoid_table OUT.inc   (65536 comma-separated uint32 bit patterns)
+// Only 8192 of the 65536 values need a table.  For a BF16 bit pattern b with
+// biased exponent field e:
+//   e <  102 (|g| < 2^-25, zeros and subnormals included): sigma32 = g * 0.5
+//            (g/2 is exact in binary32 and g^2/4 is below half an ulp of it);
+//   e >= 134 (|g| >= 2^7), g > 0: sigma32 = g (exp(-g) < 2^-184);
+//   e >= 134, g < 0: sigma32 = -0 (|g| e^g < 2^-149);
+//   e == 255 (Inf, NaN): 0 (the library defines no value for them);
+//   102 <= e < 134: entry ((b >> 15) << 12) | ((e - 102) << 7) | (b & 127).
+// The program checks this rule against the full evaluation for every pattern
+// and fails (exit status 1) on any difference.
+//
+// Usage: gen_sigmoid_table OUT.inc   (8192 comma-separated uint32 bit patterns)
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -62,17 +73,40 @@ static float sigmoid_times_input(float gf) {
     return (float)(g / (1.0 + e));
 }
 
+static uint32_t full_value(uint32_t b) {
+    const float g = bits_to_float(b << 16);
+    return float_to_bits(std::isfinite(g) ? sigmoid_times_input(g) : 0.0f);
+}
+
+// The rule of the header comment, given the compact table.
+static uint32_t by_rule(uint32_t b, const uint32_t *compact) {
+    const uint32_t e = (b >> 7) & 0xFFu;
+    const float g = bits_to_float(b << 16);
+    if (e < 102u) return float_to_bits(g * 0.5f);
+    if (e < 134u) return compact[((b >> 15) << 12) | ((e - 102u) << 7) | (b & 127u)];
+    if (e == 255u) return 0u;
+    return (b & 0x8000u) ? 0x80000000u : float_to_bits(g);
+}
+
 int main(int argc, char **argv) {
     if (argc != 2) {
         std::fprintf(stderr, "usage: %s OUT.inc\n", argv[0]);
         return 2;
     }
+    static uint32_t compact[8192];
+    for (uint32_t i = 0; i < 8192u; ++i) {
+        const uint32_t sign = i >> 12, e = 102u + ((i >> 7) & 31u), m = i & 127u;
+        compact[i] = full_value((sign << 15) | (e << 7) | m);
+    }
+    for (uint32_t b = 0; b < 65536u; ++b) {
+        if (by_rule(b, compact) != full_value(b)) {
+            std::fprintf(stderr, "rule differs from the full evaluation at BF16 pattern 0x%04x\n", b);
+            return 1;
+        }
+    }
     std::FILE *f = std::fopen(argv[1], "w");
     if (!f) return 1;
-    for (uint32_t b = 0; b < 65536u; ++b) {
-        const float g = bits_to_float(b << 16);
-        const float s = std::isfinite(g) ? sigmoid_times_input(g) : 0.0f;
-        std::fprintf(f, "0x%08xu,%s", float_to_bits(s), (b % 8 == 7) ? "\n" : "");
-    }
+    for (uint32_t i = 0; i < 8192u; ++i)
+        std::fprintf(f, "0x%08xu,%s", compact[i], (i % 8 == 7) ? "\n" : "");
     return std::fclose(f) == 0 ? 0 : 1;
 }

@@ -80,15 +80,39 @@ __device__ __forceinline__ float quot_f32(float x, float S) {
 
 // Per-row parameters of the quantizer.
 struct RowQ {
-    float d;   // row scale
-    float D;   // fl32(6 d)
+    float d;    // row scale
+    float D;    // fl32(6 d)
+    double rD;  // RN64(1 / D), used by the BF16-exact encoder (0 when d == 0)
 };
 
 __device__ __forceinline__ RowQ row_params(float amax) {
     RowQ r;
     r.d = amax / 2688.0f;  // correctly rounded binary32 division (HIP default)
     r.D = 6.0f * r.d;
+    r.rD = r.d == 0.0f ? 0.0 : 1.0 / (double)r.D;
     return r;
+}
+
+// Two BF16 values per 32-bit word: packed 16-bit integer helpers.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+}
+
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
+}
+
+// max |x| over 16 finite BF16 values packed two per word (low half first):
+// for finite values the magnitude order is the integer order of the low 15
+// bits, so the maximum is taken on the packed words and widened once.
+__device__ __forceinline__ float amax16_packed(const uint32_t w[8]) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = pk_max_u16(m, w[j] & 0x7FFF7FFFu);
+    return __uint_as_float(max(m & 0xFFFFu, m >> 16) << 16);
 }
 
 // Encode one block of 16 BF16-exact values v[0..15] (FP32 registers) given
@@ -109,7 +133,10 @@ __device__ __forceinline__ void encode_block16(const float v[16], float bamax, R
         codes_hi = w[1];
         return;
     }
-    float t = bamax / rq.D;  // correctly rounded
+    // fl32(bamax / D): bamax is one of the block's magnitudes, so for BF16
+    // inputs the binary64 product with RN64(1/D) rounds to the same value
+    // (see quot_bf16); otherwise a correctly rounded binary32 division.
+    const float t = kBF16Exact ? quot_bf16(bamax, rq.rD) : bamax / rq.D;
     uint32_t sb = e4m3_encode_sat(t);
     scale_byte = sb;
     float S = e4m3_to_f32(sb) * rq.d;

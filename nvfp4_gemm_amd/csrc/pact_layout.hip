@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void transpose_quant_kernel(const uint8_t *cod
     RowQ rq;
     rq.d = rowd[kl];
     rq.D = rowD[kl];
+    rq.rD = 0.0;  // unused by the binary32 encoder
     uint32_t lo, hi, sb;
     encode_block16<false>(v, bmax, rq, lo, hi, sb);
     u32x2 c;
