@@ -150,8 +150,13 @@ pact_status pact_build_weight_layouts(const uint16_t *W, const pact_nvfp4 *W_fwd
                                       const pact_nvfp4 *W_bwd, void *ws, size_t ws_bytes,
                                       void *stream);
 
-/* Workspace bytes the GEMMs need for M rows, output width N, contraction K and
- * LoRA rank r (0 when r == 0). */
+/* Workspace bytes the GEMMs of one projection need (forward: output [M][N]
+ * over K; input gradient: [M][K] over N) with LoRA rank r: the LoRA-down
+ * product [M][r rounded up to 16] BF16, then room for FP32 partial sums when
+ * the launch plan splits K across workgroups (small outputs with long K).
+ * A GEMM given less than this but at least the LoRA-down product runs
+ * without the K split; results are within the same tolerance either way and
+ * bit-identical across runs with the same workspace size. */
 size_t pact_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /* Forward NVFP4 GEMM of one frozen projection plus its BF16 LoRA term
@@ -180,6 +185,14 @@ pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16_t *dY, int
  * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
  * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */
 pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64_t n, void *stream);
+
+/* Diagnostic: the launch plan of a GEMM with output [M][N] contracted over K
+ * on the current device (host only, no GPU work): *kernel = 0 for the
+ * 256 x 256 single-decode kernel, 1-4 for the main kernel with wavefronts
+ * (2,2,1), (2,1,2), (1,2,2), (1,1,4); *ks = number of K ranges split across
+ * workgroups (1: no split).  PACT_ERR_INVALID_ARG for negative sizes or null
+ * outputs. */
+pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t *kernel, int32_t *ks);
 
 #ifdef __cplusplus
 }

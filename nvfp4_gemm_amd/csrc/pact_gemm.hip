@@ -52,6 +52,8 @@ struct GemmArgs {
     const uint16_t *C;  // nullable, leading dim ldy
     uint16_t *Y;
     int64_t ldy;
+    int ks;       // K ranges split across workgroups (blockIdx.y); 1: no split
+    float *part;  // ks > 1: FP32 partial fragments [ks][ceil(M/32)][ceil(N/32)][1024]
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -250,6 +252,39 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
     });
 }
 
+// Split-K: a workgroup stores its FP32 partial fragments instead of running
+// the epilogue; fragment (i, j) of split s is 1024 floats at
+// part + ((s FM + i) FN + j) 1024, element e of lane l at (e / 4) 256 + 4 l +
+// e % 4 (every store instruction writes 1 KB contiguously).  Fragments past
+// the output are not stored.
+template <int F, typename AccFn>
+__device__ __forceinline__ void store_partials(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
+                                               const int (&nb)[F]) {
+    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5;
+    static_for<F>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int fi = mb[i] >> 5, fj = nb[i] >> 5;
+        if (fi < FM && fj < FN) {
+            float *dst = p.part + (((int64_t)blockIdx.y * FM + fi) * FN + fj) * 1024 + 4 * lane;
+            const float16_t &a = accf(ic);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<float4_t *>(dst + 256 * e4) =
+                    float4_t{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
+        }
+    });
+}
+
+// End of a main kernel: the epilogue, or (split K) the partial store.
+template <bool SPLIT, int F, int G, typename AccFn>
+__device__ __forceinline__ void finish_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
+                                             const int (&nb)[F]) {
+    if constexpr (SPLIT)
+        store_partials<F>(p, lane, accf, mb, nb);
+    else
+        epi_frags<F, G>(p, lane, accf, mb, nb);
+}
+
 // Main kernel.  Every wavefront owns a 128 x 128 accumulator tile (4 x 4
 // fragments of 32 x 32, 256 FP32 per lane) and decodes its own MFMA operands
 // from the packed NVFP4 stage in LDS: per K16 step it converts 8 fragments
@@ -307,7 +342,7 @@ struct GemmShape {
     static_assert(N_CODE_I % G == 0 && N_SC_I % G == 0, "loads split evenly");
 };
 
-template <int WM, int WN, int WK, bool KFULL>
+template <int WM, int WN, int WK, bool KFULL, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     using SH = GemmShape<WM, WN, WK>;
     constexpr int G = SH::G, BM = SH::BM, BN = SH::BN, ROWS = SH::ROWS;
@@ -328,8 +363,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
     const int nblk = K >> 4;
-    const int S = ((K + kSK - 1) / kSK) / WK;  // stages per group (the host makes it exact)
-    const int gs0 = grp * S;                    // first global stage of this group
+    // stages per group (the host makes it exact); workgroup blockIdx.y of a
+    // split-K launch takes the y-th of ks equal ranges of stages
+    const int S = ((K + kSK - 1) / kSK) / (WK * p.ks);
+    const int gs0 = ((int)blockIdx.y * WK + grp) * S;  // first global stage of this group
     uint8_t *const glds = lds + grp * SH::GROUP_BYTES;
 
     // ---- per-wavefront load assignment: load q of a stage ----
@@ -558,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             mbs[i] = mw + 32 * (i >> 2);
             nbs[i] = nw + 32 * (i & 3);
         }
-        epi_frags<16, 4>(p, lane, [&](auto ic) -> float16_t & {
+        finish_frags<SPLIT, 16, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return acc[i >> 2][i & 3];
         }, mbs, nbs);
@@ -599,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
                 mbs[4 * i + c] = mw + 32 * (grp * ROWS_PER_OWNER + i);
                 nbs[4 * i + c] = nw + 32 * c;
             }
-        epi_frags<NF, 4>(p, lane, [&](auto ic) -> float16_t & {
+        finish_frags<SPLIT, NF, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return own[i >> 2][i & 3];
         }, mbs, nbs);
@@ -643,6 +680,7 @@ __device__ __forceinline__ void wait_vmcnt_lds_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     using SH = Gemm8Shape;
     constexpr int STAGE = SH::STAGE, PCODE = SH::PCODE, FPH = SH::FPH, LPW = SH::LPW;
@@ -661,7 +699,8 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     const int m0 = tm * SH::BM, n0 = tn * SH::BN;
     const int K = p.K;
     const int nblk = K >> 4;
-    const int S = K / kSK;  // stages (K % 64 == 0 for this kernel)
+    const int S = (K / kSK) / p.ks;  // stages (K % 64 == 0 for this kernel; the host makes it exact)
+    const int s0 = (int)blockIdx.y * S;  // first stage of this workgroup's K range
 
     // ---- stage loads: wavefront w issues code loads w (A rows 32w..) and
     // w + 8 (B rows), and scale load w (rows 64w.., A when w < 4) ----
@@ -689,11 +728,11 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
         uint8_t *const buf = ring + (s % kNBuf) * STAGE;
         const bool live = s < S;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_ac : rs_none, (lds_void_t *)(buf + wave * 1024), 16,
-                                                 (int)off_a, s * (kSK / 2), 0, 0);
+                                                 (int)off_a, (s0 + s) * (kSK / 2), 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_bc : rs_none, (lds_void_t *)(buf + (wave + 8) * 1024),
-                                                 16, (int)off_b, s * (kSK / 2), 0, 0);
+                                                 16, (int)off_b, (s0 + s) * (kSK / 2), 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rs_sc : rs_none, (lds_void_t *)(buf + PCODE + wave * 256), 4,
-                                                 (int)off_s, s * (kSK / 16), 0, 0);
+                                                 (int)off_s, (s0 + s) * (kSK / 16), 0, 0);
     };
 
     // ---- decode: thread t owns tile row t; phase q = half (q & 1) of stage q/2 ----
@@ -814,10 +853,41 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
         mbs[i] = mw + 32 * (i >> 1);
         nbs[i] = nw + 32 * (i & 1);
     }
-    epi_frags<8, 2>(p, lane, [&](auto ic) -> float16_t & {
+    finish_frags<SPLIT, 8, 2>(p, lane, [&](auto ic) -> float16_t & {
         constexpr int i = decltype(ic)::value;
         return acc[i >> 1][i & 1];
     }, mbs, nbs);
+}
+
+// Split-K epilogue: wavefront w takes output fragment (w / FN, w % FN), adds
+// the ks partials in split order (s = 0, 1, ...; the same order on every
+// run) and runs the epilogue on the sum.
+__global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
+    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5;
+    const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (w >= FM * FN) return;  // whole wavefronts
+    const int lane = threadIdx.x & 63;
+    const int fi = w / FN, fj = w - fi * FN;
+    const int64_t fstride = (int64_t)FM * FN * 1024;
+    const float *src = p.part + ((int64_t)fi * FN + fj) * 1024 + 4 * lane;
+    float16_t acc;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        const float4_t v = *reinterpret_cast<const float4_t *>(src + 256 * e4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[4 * e4 + q] = v[q];
+    }
+    for (int s = 1; s < p.ks; ++s) {
+        const float *ps = src + s * fstride;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4_t v = *reinterpret_cast<const float4_t *>(ps + 256 * e4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[4 * e4 + q] = acc[4 * e4 + q] + v[q];
+        }
+    }
+    const int mbs[1] = {32 * fi}, nbs[1] = {32 * fj};
+    epi_frags<1, 1>(p, lane, [&](auto) -> float16_t & { return acc; }, mbs, nbs);
 }
 
 // ---- LoRA down-projection --------------------------------------------------
@@ -889,61 +959,124 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int6
     }
 }
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
-    (void)N;
-    (void)K;
+// ---- launch plan ------------------------------------------------------------
+// Kernel: 0 = the 256 x 256 kernel (K % 64 == 0), 1..4 = the main kernel with
+// wavefronts (WM, WN, WK) = (2,2,1), (2,1,2), (1,2,2), (1,1,4).  ks: K ranges
+// split across workgroups, summed by the split-K epilogue kernel.
+struct GemmPlan {
+    int kernel;
+    int ks;
+};
+
+struct KernelShape {
+    int bm, bn, wk;
+    // cost model fitted to measured launches (MI355X, 256 CUs): per-workgroup
+    // rate with the whole chip busy and with it nearly idle (TFLOP/s per CU),
+    // fixed cost per round of workgroups (pipeline fill, epilogue; us)
+    double rate_full, rate_idle, fixed_us;
+};
+static constexpr KernelShape kKernels[5] = {{256, 256, 1, 3.74, 7.64, 19.4},
+                                            {256, 256, 1, 3.71, 6.11, 20.1},
+                                            {256, 128, 2, 3.61, 4.86, 15.3},
+                                            {128, 256, 2, 3.70, 4.98, 15.5},
+                                            {128, 128, 4, 3.25, 3.64, 10.9}};
+static constexpr double kPartialTBs = 12.6;  // partials out and back (MALL-resident)
+static constexpr double kSplitEpiUs = 0.5;   // the extra epilogue launch
+
+static size_t partial_bytes(int64_t M, int64_t N, int ks) {
+    if (ks <= 1) return 0;
+    return (size_t)ks * (size_t)((M + 31) / 32) * (size_t)((N + 31) / 32) * 4096u;
+}
+
+// Estimated duration (microseconds): a fixed cost per round of one
+// workgroup per CU, plus the FLOPs of the workgroups spread over the CUs at
+// a rate that rises as fewer CUs are busy (clock headroom); a K split adds
+// the partials' round trip and the epilogue launch.
+static double plan_cost(int64_t M, int64_t N, int64_t K, int kernel, int ks, int cus) {
+    const KernelShape &k = kKernels[kernel];
+    const int64_t wgs = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * ks;
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const double fill = (double)(wgs < cus ? wgs : cus) / cus;
+    const double rate = k.rate_full + (k.rate_idle - k.rate_full) * (1.0 - fill);
+    const double wg_flop = 2.0 * k.bm * k.bn * (double)K / ks;
+    const double spread = (double)wgs / cus > 1.0 ? (double)wgs / cus : 1.0;
+    double t = (double)rounds * k.fixed_us + spread * wg_flop / (rate * 1e6);
+    if (ks > 1) t += 2.0 * (double)partial_bytes(M, N, ks) / (kPartialTBs * 1e6) + kSplitEpiUs;
+    return t;
+}
+
+static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cus) {
+    const int64_t ns = (K + kSK - 1) / kSK;
+    GemmPlan best = {1, 1};
+    double best_cost = 1e300;
+    for (int kernel = 0; kernel < 5; ++kernel) {
+        if (kernel == 0 && K % kSK != 0) continue;
+        const int wk = kKernels[kernel].wk;
+        for (int ks : {1, 2, 3, 4, 6, 8, 12, 16}) {
+            if (ks > 1 && K % kSK != 0) break;       // ragged K: no split
+            if (ns % ((int64_t)wk * ks) != 0) continue;
+            if (ks > 1 && ns / ((int64_t)wk * ks) < 2) continue;  // at least two stages per wavefront
+            const double c = plan_cost(M, N, K, kernel, ks, cus);
+            if (c < best_cost) {
+                best_cost = c;
+                best = {kernel, ks};
+            }
+        }
+    }
+    return best;
+}
+
+static size_t lora_ws_bytes(int64_t M, int32_t r) {
     if (r <= 0) return 0;
-    const int64_t rpad = round_up(r, 16);
-    return (size_t)round_up(M * rpad * 2, 256);
+    return (size_t)round_up(M * round_up(r, 16) * 2, 256);
+}
+
+// Workspace of one projection: the LoRA-down product and the split-K
+// partials of either direction (forward [M][N] over K, input gradient
+// [M][K] over N).
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+    const int cus = device_cus();
+    const GemmPlan f = plan_gemm(M, N, K, cus), b = plan_gemm(M, K, N, cus);
+    const size_t pf = partial_bytes(M, N, f.ks), pb = partial_bytes(M, K, b.ks);
+    return lora_ws_bytes(M, r) + (pf > pb ? pf : pb);
 }
 
 template <int WM, int WN, int WK>
 static void launch_gemm_cfg(const GemmArgs &a, hipStream_t st) {
     using SH = GemmShape<WM, WN, WK>;
     const int tiles = ((a.M + SH::BM - 1) / SH::BM) * ((a.N + SH::BN - 1) / SH::BN);
-    if (a.K % kSK == 0)
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, true>), dim3(tiles), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)tiles, (unsigned)a.ks);
+    if (a.ks > 1)  // the plan splits K only when K % 64 == 0
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, true, true>), grid, dim3(256), 0, st, a);
+    else if (a.K % kSK == 0)
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, true, false>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, false>), dim3(tiles), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, false, false>), grid, dim3(256), 0, st, a);
 }
 
-// Wavefront arrangement: the estimated duration is the number of rounds of
-// one workgroup per CU times a wavefront's share of K, plus the partial-sum
-// exchange (about one stage for a 2-way K split, one and a half for 4-way).
-static pact_status run_gemm(const GemmArgs &a, hipStream_t st) {
-    const int64_t ns = (a.K + kSK - 1) / kSK;
-    const int cus = device_cus();
-    struct Cand {
-        int wm, wn, wk;
-    };
-    const Cand cands[4] = {{2, 2, 1}, {2, 1, 2}, {1, 2, 2}, {1, 1, 4}};
-    int best = 0;
-    double best_cost = 0.0;
-    for (int c = 0; c < 4; ++c) {
-        const Cand &k = cands[c];
-        if (ns % k.wk != 0) continue;
-        const int64_t tiles = ((a.M + 128 * k.wm - 1) / (128 * k.wm)) * ((a.N + 128 * k.wn - 1) / (128 * k.wn));
-        const int64_t rounds = (tiles + cus - 1) / cus;
-        const double cost = (double)rounds * ((double)(ns / k.wk) + (k.wk == 2 ? 1.0 : k.wk == 4 ? 1.5 : 0.0));
-        if (c == 0 || cost < best_cost) {
-            best = c;
-            best_cost = cost;
-        }
-    }
-    switch (best) {
-        case 0:
-            if (a.K % kSK == 0) {
-                const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-                hipLaunchKernelGGL(gemm8_kernel, dim3(tiles), dim3(512), 0, st, a);
-            } else {
-                launch_gemm_cfg<2, 2, 1>(a, st);
-            }
+static pact_status launch_plan(const GemmArgs &a, int kernel, hipStream_t st) {
+    switch (kernel) {
+        case 0: {
+            const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+            const dim3 grid((unsigned)tiles, (unsigned)a.ks);
+            if (a.ks > 1)
+                hipLaunchKernelGGL(gemm8_kernel<true>, grid, dim3(512), 0, st, a);
+            else
+                hipLaunchKernelGGL(gemm8_kernel<false>, grid, dim3(512), 0, st, a);
             break;
-        case 1: launch_gemm_cfg<2, 1, 2>(a, st); break;
-        case 2: launch_gemm_cfg<1, 2, 2>(a, st); break;
+        }
+        case 1: launch_gemm_cfg<2, 2, 1>(a, st); break;
+        case 2: launch_gemm_cfg<2, 1, 2>(a, st); break;
+        case 3: launch_gemm_cfg<1, 2, 2>(a, st); break;
         default: launch_gemm_cfg<1, 1, 4>(a, st); break;
     }
-    return launch_status();
+    PACT_TRY(launch_status());
+    if (a.ks > 1) {
+        const int64_t frags = ((int64_t)(a.M + 31) / 32) * ((a.N + 31) / 32);
+        hipLaunchKernelGGL(splitk_epi_kernel, dim3((unsigned)((frags + 3) / 4)), dim3(256), 0, st, a);
+        PACT_TRY(launch_status());
+    }
+    return PACT_OK;
 }
 
 // Shared body of the forward and input-gradient entry points.
@@ -990,11 +1123,20 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     a.C = C;
     a.Y = Y;
     a.ldy = ldy;
+    const size_t t_bytes = lora_ws_bytes(M, r);
+    if (r > 0) {
+        if (!ws || ws_bytes < t_bytes) return PACT_ERR_WORKSPACE;
+        if (!aligned16(ws)) return PACT_ERR_MISALIGNED;
+    }
+    // K split across workgroups when the plan asks for it and the workspace
+    // holds the partials (after the LoRA-down product); otherwise one pass
+    GemmPlan plan = plan_gemm(M, Nout, Kc, device_cus());
+    const size_t p_bytes = partial_bytes(M, Nout, plan.ks);
+    if (plan.ks > 1 && (!ws || !aligned16(ws) || ws_bytes < t_bytes + p_bytes)) plan.ks = 1;
+    a.ks = plan.ks;
+    a.part = plan.ks > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + t_bytes) : nullptr;
     if (r > 0) {
         const int rpad = (int)round_up(r, 16);
-        const size_t need = gemm_ws_bytes(M, Nout, Kl, r);
-        if (!ws || ws_bytes < need) return PACT_ERR_WORKSPACE;
-        if (!aligned16(ws)) return PACT_ERR_MISALIGNED;
         uint16_t *T = static_cast<uint16_t *>(ws);
         hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(64 * kDownWaves), 0, st,
                            Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, lora->scale, T);
@@ -1006,12 +1148,20 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
         a.r = r;
         a.rpad = rpad;
     }
-    return run_gemm(a, st);
+    return launch_plan(a, plan.kernel, st);
 }
 
 }  // namespace pact
 
 using namespace pact;
+
+extern "C" pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t *kernel, int32_t *ks) {
+    if (M < 0 || N < 0 || K < 0 || !kernel || !ks) return PACT_ERR_INVALID_ARG;
+    const GemmPlan plan = plan_gemm(M, N, K, device_cus());
+    *kernel = plan.kernel;
+    *ks = plan.ks;
+    return PACT_OK;
+}
 
 extern "C" size_t pact_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
     if (M < 0 || N < 0 || K < 0) return 0;

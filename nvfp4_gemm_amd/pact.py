@@ -38,7 +38,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_rmsnorm_quant_nvfp4", "pact_silu_mul_quant_nvfp4",
            "pact_build_weight_layouts_workspace", "pact_build_weight_layouts",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
-           "pact_debug_sigmoid32"]
+           "pact_debug_sigmoid32", "pact_debug_gemm_plan"]
 
 
 class PactError(RuntimeError):
@@ -79,6 +79,9 @@ def lib():
         L.pact_gemm_nvfp4_dgrad.argtypes = gemm_args
         L.pact_debug_sigmoid32.restype = st
         L.pact_debug_sigmoid32.argtypes = [P, P, I64, P]
+        L.pact_debug_gemm_plan.restype = st
+        L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int32)]
         _lib = L
     return _lib
 
@@ -239,9 +242,10 @@ def _gemm(fn, name, aq, Xl, bq, lora, C, out, ws, stream):
     if out is None:
         out = torch.empty((M, Nout), dtype=torch.bfloat16, device=aq.codes.device)
     r = lora.r if lora is not None else 0
-    if ws is None and r > 0:
+    if ws is None:
         need = pact_gemm_workspace(M, Nout, aq.cols, r)
-        ws = torch.empty((need,), dtype=torch.uint8, device=aq.codes.device)
+        if need > 0:
+            ws = torch.empty((need,), dtype=torch.uint8, device=aq.codes.device)
     da, db = aq.desc(), bq.desc()
     dl = lora.desc() if lora is not None else None
     _check(fn(ctypes.byref(da), _ptr(Xl), _ld(Xl) if Xl is not None else 0, ctypes.byref(db),
@@ -269,3 +273,10 @@ def pact_debug_sigmoid32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:
     _check(lib().pact_debug_sigmoid32(_ptr(g_bits), _ptr(out), g_bits.numel(), _stream(stream)),
            "pact_debug_sigmoid32")
     return out
+
+
+def pact_debug_gemm_plan(M: int, N: int, K: int) -> tuple[int, int]:
+    """(kernel, ks) of the GEMM launch plan for output [M][N] over K."""
+    k, ks = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pact_debug_gemm_plan(M, N, K, ctypes.byref(k), ctypes.byref(ks)), "pact_debug_gemm_plan")
+    return k.value, ks.value

@@ -117,3 +117,23 @@ def test_gemm_validation(L):
     dyq, wb = _nv(rows=M, cols=N), _nv(rows=K, cols=N)
     assert dg(ctypes.byref(dyq), None, 0, ctypes.byref(_nv(rows=K, cols=K)), None, None, FAKE, K, None, 0, None) == 1
     assert dg(ctypes.byref(dyq), FAKE, N, ctypes.byref(wb), ctypes.byref(lo), None, FAKE, K, None, 0, None) == 4
+
+
+def test_gemm_plan_host_logic(L):
+    """The launch plan (host logic, no GPU work): large outputs run in one
+    pass; a small output with long K splits K, and the workspace query then
+    covers the FP32 partials of either direction."""
+    k, ks = ctypes.c_int32(), ctypes.c_int32()
+    assert L.pact_debug_gemm_plan(-1, 8, 8, ctypes.byref(k), ctypes.byref(ks)) == 1
+    assert L.pact_debug_gemm_plan(8, 8, 8, None, ctypes.byref(ks)) == 1
+    assert L.pact_debug_gemm_plan(8192, 8192, 3072, ctypes.byref(k), ctypes.byref(ks)) == 0
+    assert ks.value == 1
+    assert L.pact_debug_gemm_plan(1024, 512, 2048, ctypes.byref(k), ctypes.byref(ks)) == 0
+    assert ks.value > 1 and 0 <= k.value <= 4
+    split = ks.value
+    parts = split * (1024 // 32) * (512 // 32) * 4096
+    assert L.pact_gemm_workspace(1024, 512, 2048, 0) >= parts
+    assert L.pact_gemm_workspace(1024, 512, 2048, 16) >= parts + 2 * 16 * 1024
+    assert L.pact_gemm_workspace(1024, 2048, 512, 16) >= parts + 2 * 16 * 1024  # the input-gradient direction
+    assert L.pact_debug_gemm_plan(100, 200, 520, ctypes.byref(k), ctypes.byref(ks)) == 0
+    assert ks.value == 1  # K % 64 != 0: no split

@@ -105,6 +105,40 @@ def test_gemm_layer_sizes_sampled_rows(M, N, K, r):
     _run_pair(M, N, K, r, seed=3, with_c=True, rows=rows)
 
 
+@pytest.mark.parametrize("M,N,K,r", [(1024, 512, 2048, 16), (1024, 2048, 8192, 16), (1000, 528, 2048, 8),
+                                     (256, 512, 1024, 8)])
+def test_gemm_split_k(M, N, K, r):
+    """Shapes whose launch plan splits K across workgroups (FP32 partials
+    summed in split order by a second kernel), including ragged M and N."""
+    assert max(pb.pact_debug_gemm_plan(M, N, K)[1], pb.pact_debug_gemm_plan(M, K, N)[1]) > 1
+    rows = np.unique(np.concatenate([[0, 1, M - 1], np.arange(5, M, max(1, M // 24))]))
+    _run_pair(M, N, K, r, seed=17, with_c=True, rows=rows)
+
+
+def test_gemm_split_k_workspace_fallback():
+    """A workspace holding only the LoRA-down product runs the GEMM in one
+    pass; both paths meet the tolerance and each is deterministic."""
+    M, N, K, r = 1024, 512, 2048, 16
+    assert pb.pact_debug_gemm_plan(M, N, K)[1] > 1
+    li = synth.single_linear_inputs(M=M, N=N, K=K, r=r, seed=23, act="t4", outliers=True)
+    A, B, lora = _lora(li, r)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(3, M, 41)]))
+    xq = oracle.quantize_bf16(li.X)
+    f, _ = oracle.build_weight_layouts(li.W)
+    Y = oracle.gemm_fwd(xq, li.X, f, A, B, li.s, None, rows=rows)
+    gf, _ = pb.pact_build_weight_layouts(G.dev_bf16(li.W))
+    gxq = pb.pact_quantize_nvfp4(G.dev_bf16(li.X))
+    X = G.dev_bf16(li.X)
+    full = torch.empty((pb.pact_gemm_workspace(M, N, K, r),), dtype=torch.uint8, device="cuda")
+    small = torch.empty((M * 16 * 2,), dtype=torch.uint8, device="cuda")  # the [M][16] BF16 product only
+    assert small.numel() < full.numel()
+    outs = [pb.pact_gemm_nvfp4_fwd(gxq, gf, X=X, lora=lora, ws=w) for w in (full, small, full, small)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+    for o, name in ((outs[0], "split"), (outs[1], "one pass")):
+        G.check_gemm_tolerance(G.host_bits(o)[rows], Y, f"fwd {name}")
+
+
 def test_lora_identity_and_alias():
     """B = 0 reproduces the frozen-only output; C may alias Y."""
     M, N, K, r = 96, 160, 256, 16
