@@ -897,14 +897,21 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
 // this equals s . bf16(X P^T) exactly, i.e. the scale applied after the
 // rank-r product.
 // One workgroup of 16 wavefronts per 16 rows: each wavefront takes a slice of
-// K, and the 16 partial tiles are summed through LDS in a fixed order.
+// K and computes RG groups of 16 ranks from one pass over its slice of X (the
+// BF16 activations are the kernel's HBM traffic), and the 16 partial tiles
+// are summed through LDS in a fixed order.  Ranks beyond 16 RG take further
+// passes (r > 64 only).
 constexpr int kDownWaves = 16;
-constexpr int kDownU = 8;
+// K32 chunks whose loads are in flight together (fewer with more rank groups:
+// a 1024-thread workgroup has 128 VGPRs per thread)
+template <int RG>
+constexpr int down_chunks() { return RG == 1 ? 8 : RG == 2 ? 6 : 4; }
 
+template <int RG>
 __global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int64_t ldx, int M, int Kl,
                                                          const uint16_t *Ps, int64_t p_sj, int64_t p_sk,
-                                                         int r, int rpad, float scale, uint16_t *T) {
-    __shared__ float red[kDownWaves][16][17];
+                                                         int r, int rpad, int j0, float scale, uint16_t *T) {
+    __shared__ float red[kDownWaves][16][16 * RG + 1];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int m0 = blockIdx.x * 16;
@@ -912,51 +919,78 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int6
     const int kg = 8 * (lane >> 4);
     const int ks = ((Kl + kDownWaves - 1) / kDownWaves + 31) / 32 * 32;
     const int kb = w * ks, ke = min(Kl, kb + ks);
-    for (int f = 0; f < rpad / 16; ++f) {
-        const int j = 16 * f + (lane & 15);
-        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        // kDownU chunks of 32 K per iteration: all their loads are issued
-        // before the MFMAs, so the loop is not bound by one load latency per chunk
-        for (int k0 = kb; k0 < ke; k0 += 32 * kDownU) {
-            u32x4 va[kDownU], vb[kDownU];
+    const uint16_t *xr = X + (int64_t)row * ldx;
+    float4_t acc[RG];
 #pragma unroll
-            for (int u = 0; u < kDownU; ++u) {
-                const int k = k0 + 32 * u + kg;
-                va[u] = u32x4{0u, 0u, 0u, 0u};
-                vb[u] = u32x4{0u, 0u, 0u, 0u};
-                if (k < ke) {
-                    va[u] = *reinterpret_cast<const u32x4 *>(X + (int64_t)row * ldx + k);
+    for (int f = 0; f < RG; ++f) acc[f] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // U chunks of 32 K per iteration: all their loads are issued before the
+    // MFMAs, so the loop is not bound by one load latency per chunk
+    constexpr int U = down_chunks<RG>();
+    for (int k0 = kb; k0 < ke; k0 += 32 * U) {
+        u32x4 va[U], vb[U][RG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 32 * u + kg;
+            va[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int f = 0; f < RG; ++f) vb[u][f] = u32x4{0u, 0u, 0u, 0u};
+            if (k < ke) {
+                va[u] = *reinterpret_cast<const u32x4 *>(xr + k);
+#pragma unroll
+                for (int f = 0; f < RG; ++f) {
+                    const int j = j0 + 16 * f + (lane & 15);
                     if (j < r) {
                         if (p_sk == 1) {
-                            vb[u] = *reinterpret_cast<const u32x4 *>(Ps + (int64_t)j * p_sj + k);
+                            vb[u][f] = *reinterpret_cast<const u32x4 *>(Ps + (int64_t)j * p_sj + k);
                         } else {
                             uint32_t t[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 t[e] = (uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e) * p_sk] |
                                        ((uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e + 1) * p_sk] << 16);
-                            vb[u] = u32x4{t[0], t[1], t[2], t[3]};
+                            vb[u][f] = u32x4{t[0], t[1], t[2], t[3]};
                         }
                     }
                 }
             }
-#pragma unroll
-            for (int u = 0; u < kDownU; ++u)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[u]),
-                                                              __builtin_bit_cast(bf16x8_t, vb[u]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[w][4 * (lane >> 4) + e][lane & 15] = acc[e];
-        __syncthreads();
-        if (threadIdx.x < 256) {
-            const int mi = threadIdx.x >> 4, ji = threadIdx.x & 15;
-            float sum = 0.0f;
-            for (int q = 0; q < kDownWaves; ++q) sum += red[q][mi][ji];
-            const float ts = scale * sum;
-            if (m0 + mi < M) T[(int64_t)(m0 + mi) * rpad + 16 * f + ji] = (uint16_t)f32_to_bf16_bits(ts);
-        }
-        __syncthreads();
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int f = 0; f < RG; ++f)
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[u]),
+                                                                 __builtin_bit_cast(bf16x8_t, vb[u][f]), acc[f], 0,
+                                                                 0, 0);
     }
+#pragma unroll
+    for (int f = 0; f < RG; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[w][4 * (lane >> 4) + e][16 * f + (lane & 15)] = acc[f][e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * 16 * RG; i += 1024) {
+        const int mi = i / (16 * RG), ji = i % (16 * RG);
+        float sum = 0.0f;
+        for (int q = 0; q < kDownWaves; ++q) sum += red[q][mi][ji];
+        const float ts = scale * sum;
+        if (m0 + mi < M) T[(int64_t)(m0 + mi) * rpad + j0 + ji] = (uint16_t)f32_to_bf16_bits(ts);
+    }
+}
+
+static pact_status launch_lora_down(const uint16_t *X, int64_t ldx, int M, int Kl, const uint16_t *Ps,
+                                    int64_t p_sj, int64_t p_sk, int r, int rpad, float scale, uint16_t *T,
+                                    hipStream_t st) {
+    const dim3 grid((unsigned)((M + 15) / 16)), block(64 * kDownWaves);
+    for (int j0 = 0; j0 < rpad; j0 += 64) {
+        const int rg = (rpad - j0) / 16 < 4 ? (rpad - j0) / 16 : 4;
+        switch (rg) {
+            case 1: hipLaunchKernelGGL(lora_down_kernel<1>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
+            case 2: hipLaunchKernelGGL(lora_down_kernel<2>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
+            case 3: hipLaunchKernelGGL(lora_down_kernel<3>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
+            default: hipLaunchKernelGGL(lora_down_kernel<4>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
+        }
+        PACT_TRY(launch_status());
+    }
+    return PACT_OK;
 }
 
 // ---- launch plan ------------------------------------------------------------
@@ -1138,9 +1172,7 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     if (r > 0) {
         const int rpad = (int)round_up(r, 16);
         uint16_t *T = static_cast<uint16_t *>(ws);
-        hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(64 * kDownWaves), 0, st,
-                           Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, lora->scale, T);
-        PACT_TRY(launch_status());
+        PACT_TRY(launch_lora_down(Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, lora->scale, T, st));
         a.T = T;
         a.Qs = Qsrc;
         a.q_sn = q_sn;
