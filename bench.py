@@ -57,7 +57,10 @@ PEAK_FP4_TFLOPS = 10100.0       # context only: scaled FP4 MFMA cannot apply per
 PEAK_HBM_GBS = 8000.0
 GEMM_SOURCE = os.path.join(ROOT, "nvfp4_gemm_amd", "csrc", "pact_gemm.hip")
 CONFIGS = ["single_linear", "llama1b_layer", "qwen1.5b_layer", "llama3b_layer", "llama3b_stack28"]
-GEMM_KERNELS = ("gemm_kernel", "lora_down_kernel")
+# kernels of the GEMM entry points: LoRA-down, one main kernel, and (split K)
+# the epilogue kernel; the main kernel's name marks one entry-point call
+GEMM_KERNELS = ("gemm_kernel", "gemm8_kernel", "lora_down_kernel", "splitk_epi_kernel")
+GEMM_MAIN_KERNELS = ("gemm_kernel", "gemm8_kernel")
 
 
 def parse():
@@ -427,7 +430,7 @@ def summarize_pmc(args):
             if any(m in name for m in GEMM_KERNELS):
                 tot += v
                 disp[did] = name
-        return tot, sum(1 for n in disp.values() if "gemm_kernel" in n)
+        return tot, sum(1 for n in disp.values() if any(m in n for m in GEMM_MAIN_KERNELS))
 
     def copy_kib(d, counter):
         vals = {}
@@ -445,7 +448,7 @@ def summarize_pmc(args):
     write, nw = gemm_totals(wdir, "WRITE_SIZE")
     hbm = fetch * 1024.0 * f_fetch / nf + write * 1024.0 * f_write / nw
     lines = [
-        "# HBM traffic of the NVFP4 GEMM entry points (gemm_kernel + lora_down_kernel),",
+        "# HBM traffic of the NVFP4 GEMM entry points (LoRA-down, main and split-K epilogue kernels),",
         "# from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs, each scaled by the value",
         "# the same counter reads for a plain device copy of known size.",
         f"command: {args.pmc_command}",
