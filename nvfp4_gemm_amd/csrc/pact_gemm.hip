@@ -108,18 +108,18 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gsize;
 }
 
-// Epilogue of a 32x32 accumulator fragment whose rows start at mb and columns
+// Epilogue of 32x32 accumulator fragments whose rows start at mb and columns
 // at nb: y = fl32(fl32(acc d_a[m]) d_b[n]), then the LoRA term T_s.Q^T
 // (T_s = bf16(s . X P^T) from the down kernel) is accumulated into y by one
-// BF16 MFMA per 16 ranks, then C is added and y rounded to BF16 and stored.
-// Split in two so that callers issue the loads of several fragments before
-// finishing any of them (the epilogue is otherwise bound by one global-load
-// latency per fragment).
+// BF16 MFMA per 16 ranks (all in the MFMA accumulator layout, lane = column).
+// Then a group of horizontally adjacent fragments goes through a per-wavefront
+// LDS tile to row-major order, where C is added and y is rounded to BF16, so
+// that C is read and Y written in 16-byte chunks of 8 columns (8 lanes cover
+// 128 contiguous bytes of a row) instead of 2-byte accesses.
 struct EpiIn {
     float dx[16];    // d_a of the lane's 16 rows
     float dw;        // d_b of the lane's column
     u32x4 t[2], q[2];  // LoRA operands, ranks [0, 32) (prefetched when rpad <= 32)
-    uint32_t c[8];   // C of the lane's 16 elements, BF16 pairs
 };
 
 __device__ __forceinline__ bool epi_lora_prefetch(const GemmArgs &p) {
@@ -154,21 +154,9 @@ __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int 
             if (j0 < p.r) in.q[i] = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
         }
     }
-    if (p.C) {
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) {
-            uint32_t w = 0u;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int e = 2 * e2 + i;
-                const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < p.M && n < p.N) w |= (uint32_t)p.C[(int64_t)m * p.ldy + n] << (16 * i);
-            }
-            in.c[e2] = w;
-        }
-    }
 }
 
+// Row scales and LoRA term, in place, in the accumulator layout.
 __device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int mb, int nb, int lane,
                                            const EpiIn &in) {
     const int h = lane >> 5, lr = lane & 31;
@@ -209,14 +197,78 @@ __device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int 
                                                         __builtin_bit_cast(bf16x8_t, vb), a, 0, 0, 0);
         }
     }
-    if (n >= p.N) return;
+}
+
+// Per-wavefront LDS tile of G adjacent fragments: 32 rows of 32 G FP32 plus 4
+// of padding (lanes 32-63 of an accumulator store land 16 banks away).
+template <int G>
+constexpr int epi_tile_stride() { return 32 * G + 4; }
+template <int G>
+constexpr int epi_tile_floats() { return 32 * epi_tile_stride<G>(); }
+
+// Fragment i of the group into the tile: element e of lane (h, lr) is row
+// 8 (e / 4) + 4 h + e % 4, column 32 i + lr.
+template <int G>
+__device__ __forceinline__ void epi_to_tile(float *tile, const float16_t &a, int i, int lane) {
+    const int h = lane >> 5, lr = lane & 31;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int m = mb + 8 * (e >> 2) + 4 * h + (e & 3);
+    for (int e = 0; e < 16; ++e)
+        tile[(8 * (e >> 2) + 4 * h + (e & 3)) * epi_tile_stride<G>() + 32 * i + lr] = a[e];
+}
+
+// Row-major pass over the tile (rows mb.., columns nb0 .. nb0 + 32 G): lane l
+// takes columns 8 (l % 4G) .. +8 of rows l / 4G + 16/G q; C is loaded for all
+// of its rows first, then y = bf16(tile + C) is stored 16 bytes at a time.
+template <int G>
+__device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const float *tile, int mb, int nb0) {
+    constexpr int LPR = 4 * G;      // lanes per row
+    constexpr int RPI = 64 / LPR;   // rows per instruction
+    constexpr int NQ = 32 / RPI;    // row steps
+    const int rr = lane / LPR, c = 8 * (lane % LPR);
+    const int n = nb0 + c;
+    const bool full = n + 8 <= p.N;
+    u32x4 cv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int m = mb + RPI * q + rr;
+        cv[q] = u32x4{0u, 0u, 0u, 0u};
+        if (p.C && m < p.M) {
+            const uint16_t *src = p.C + (int64_t)m * p.ldy + n;
+            if (full) {
+                cv[q] = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (n + j < p.N) w[j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+                cv[q] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int row = RPI * q + rr;
+        const int m = mb + row;
         if (m >= p.M) continue;
-        float y = a[e];
-        if (p.C) y = y + bf16_to_f32((uint16_t)(in.c[e >> 1] >> (16 * (e & 1))));
-        p.Y[(int64_t)m * p.ldy + n] = (uint16_t)f32_to_bf16_bits(y);
+        const float4_t v0 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c);
+        const float4_t v1 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c + 4);
+        float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if (p.C) {
+            const uint32_t cw[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = y[j] + ((j & 1) ? bf16_hi(cw[j >> 1]) : bf16_lo(cw[j >> 1]));
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_bits(y[2 * j]) | (f32_to_bf16_bits(y[2 * j + 1]) << 16);
+        uint16_t *dst = p.Y + (int64_t)m * p.ldy + n;
+        if (full) {
+            *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (n + j < p.N) dst[j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+        }
     }
 }
 
@@ -231,12 +283,14 @@ __device__ __forceinline__ void static_for(Fn &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Epilogue of F fragments in groups of G: the loads of a group are issued
-// together, then the group is finished.  accf(I) returns fragment I; mb[I],
-// nb[I] its first row and column.
+// Epilogue of F fragments in groups of G horizontally adjacent fragments
+// (mb[g + i] = mb[g], nb[g + i] = nb[g] + 32 i): the loads of a group are
+// issued together, its fragments finished and written to the wavefront's LDS
+// tile (epi_tile_floats<G>() floats, not shared with other wavefronts), then
+// the group is stored row by row.  accf(I) returns fragment I.
 template <int F, int G, typename AccFn>
 __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
-                                          const int (&nb)[F]) {
+                                          const int (&nb)[F], float *tile) {
     static_assert(F % G == 0, "whole groups");
     static_for<F / G>([&](auto gc) {
         constexpr int g = decltype(gc)::value * G;
@@ -247,8 +301,15 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
         });
         static_for<G>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            epi_finish(p, accf(std::integral_constant<int, g + i>{}), mb[g + i], nb[g + i], lane, in[i]);
+            float16_t &a = accf(std::integral_constant<int, g + i>{});
+            epi_finish(p, a, mb[g + i], nb[g + i], lane, in[i]);
+            epi_to_tile<G>(tile, a, i, lane);
         });
+        // LDS operations of one wavefront complete in order; the wait keeps
+        // the compiler from treating the tile reads as independent
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        epi_rows<G>(p, lane, tile, mb[g], nb[g]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     });
 }
 
@@ -278,11 +339,11 @@ __device__ __forceinline__ void store_partials(const GemmArgs &p, int lane, AccF
 // End of a main kernel: the epilogue, or (split K) the partial store.
 template <bool SPLIT, int F, int G, typename AccFn>
 __device__ __forceinline__ void finish_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
-                                             const int (&nb)[F]) {
+                                             const int (&nb)[F], float *tile) {
     if constexpr (SPLIT)
         store_partials<F>(p, lane, accf, mb, nb);
     else
-        epi_frags<F, G>(p, lane, accf, mb, nb);
+        epi_frags<F, G>(p, lane, accf, mb, nb, tile);
 }
 
 // Main kernel.  Every wavefront owns a 128 x 128 accumulator tile (4 x 4
@@ -345,6 +406,7 @@ struct GemmShape {
 template <int WM, int WN, int WK, bool KFULL, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     using SH = GemmShape<WM, WN, WK>;
+    static_assert(SH::LDS_BYTES >= 4 * 4 * epi_tile_floats<4>(), "LDS holds the epilogue tiles");
     constexpr int G = SH::G, BM = SH::BM, BN = SH::BN, ROWS = SH::ROWS;
     constexpr int PCODE = SH::PCODE, STAGE = SH::STAGE, LPW = SH::LPW, NQC = SH::NQC;
     __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
@@ -595,10 +657,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             mbs[i] = mw + 32 * (i >> 2);
             nbs[i] = nw + 32 * (i & 3);
         }
+        if constexpr (!SPLIT) lds_barrier();  // stage buffers free for the epilogue tiles
         finish_frags<SPLIT, 16, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return acc[i >> 2][i & 3];
-        }, mbs, nbs);
+        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>());
     } else {
         // Partial tiles summed through LDS, one fragment column per round:
         // every wavefront writes its 4 fragments of the column to slot
@@ -636,10 +699,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
                 mbs[4 * i + c] = mw + 32 * (grp * ROWS_PER_OWNER + i);
                 nbs[4 * i + c] = nw + 32 * c;
             }
+        if constexpr (!SPLIT) lds_barrier();  // reduction slots free for the epilogue tiles
         finish_frags<SPLIT, NF, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return own[i >> 2][i & 3];
-        }, mbs, nbs);
+        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>());
     }
 }
 
@@ -683,6 +747,7 @@ __device__ __forceinline__ void wait_vmcnt_lds_barrier() {
 template <bool SPLIT>
 __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     using SH = Gemm8Shape;
+    static_assert(SH::LDS_BYTES >= 8 * 4 * epi_tile_floats<2>(), "LDS holds the epilogue tiles");
     constexpr int STAGE = SH::STAGE, PCODE = SH::PCODE, FPH = SH::FPH, LPW = SH::LPW;
     __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
     uint8_t *const ring = lds;
@@ -853,41 +918,52 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
         mbs[i] = mw + 32 * (i >> 1);
         nbs[i] = nw + 32 * (i & 1);
     }
+    if constexpr (!SPLIT) lds_barrier();  // every wavefront is past its last fragment reads
     finish_frags<SPLIT, 8, 2>(p, lane, [&](auto ic) -> float16_t & {
         constexpr int i = decltype(ic)::value;
         return acc[i >> 1][i & 1];
-    }, mbs, nbs);
+    }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<2>());
 }
 
-// Split-K epilogue: wavefront w takes output fragment (w / FN, w % FN), adds
-// the ks partials in split order (s = 0, 1, ...; the same order on every
-// run) and runs the epilogue on the sum.
+// Split-K epilogue: wavefront w takes the two horizontally adjacent output
+// fragments (w / FN2, 2 (w % FN2)) and (w / FN2, 2 (w % FN2) + 1), FN2 =
+// ceil(FN / 2), adds each one's ks partials in split order (s = 0, 1, ...;
+// the same order on every run) and runs the epilogue on the sums.  A second
+// fragment past the output (FN odd) reads nothing and stores nothing.
 __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
-    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5;
+    __shared__ __attribute__((aligned(16))) float tiles[4][epi_tile_floats<2>()];
+    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5, FN2 = (FN + 1) >> 1;
     const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (w >= FM * FN) return;  // whole wavefronts
+    if (w >= FM * FN2) return;  // whole wavefronts
     const int lane = threadIdx.x & 63;
-    const int fi = w / FN, fj = w - fi * FN;
+    const int fi = w / FN2, fj = 2 * (w - fi * FN2);
     const int64_t fstride = (int64_t)FM * FN * 1024;
-    const float *src = p.part + ((int64_t)fi * FN + fj) * 1024 + 4 * lane;
-    float16_t acc;
+    float16_t acc[2];
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-        const float4_t v = *reinterpret_cast<const float4_t *>(src + 256 * e4);
+    for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[4 * e4 + q] = v[q];
-    }
-    for (int s = 1; s < p.ks; ++s) {
-        const float *ps = src + s * fstride;
+        for (int e = 0; e < 16; ++e) acc[f][e] = 0.0f;
+        if (fj + f >= FN) continue;
+        const float *src = p.part + ((int64_t)fi * FN + fj + f) * 1024 + 4 * lane;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            const float4_t v = *reinterpret_cast<const float4_t *>(ps + 256 * e4);
+            const float4_t v = *reinterpret_cast<const float4_t *>(src + 256 * e4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[4 * e4 + q] = acc[4 * e4 + q] + v[q];
+            for (int q = 0; q < 4; ++q) acc[f][4 * e4 + q] = v[q];
+        }
+        for (int s = 1; s < p.ks; ++s) {
+            const float *ps = src + s * fstride;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const float4_t v = *reinterpret_cast<const float4_t *>(ps + 256 * e4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[f][4 * e4 + q] = acc[f][4 * e4 + q] + v[q];
+            }
         }
     }
-    const int mbs[1] = {32 * fi}, nbs[1] = {32 * fj};
-    epi_frags<1, 1>(p, lane, [&](auto) -> float16_t & { return acc; }, mbs, nbs);
+    const int mbs[2] = {32 * fi, 32 * fi}, nbs[2] = {32 * fj, 32 * fj + 32};
+    epi_frags<2, 2>(p, lane, [&](auto ic) -> float16_t & { return acc[decltype(ic)::value]; }, mbs, nbs,
+                    tiles[threadIdx.x >> 6]);
 }
 
 // ---- LoRA down-projection --------------------------------------------------
@@ -1106,8 +1182,8 @@ static pact_status launch_plan(const GemmArgs &a, int kernel, hipStream_t st) {
     }
     PACT_TRY(launch_status());
     if (a.ks > 1) {
-        const int64_t frags = ((int64_t)(a.M + 31) / 32) * ((a.N + 31) / 32);
-        hipLaunchKernelGGL(splitk_epi_kernel, dim3((unsigned)((frags + 3) / 4)), dim3(256), 0, st, a);
+        const int64_t pairs = ((int64_t)(a.M + 31) / 32) * (((a.N + 31) / 32 + 1) / 2);
+        hipLaunchKernelGGL(splitk_epi_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, a);
         PACT_TRY(launch_status());
     }
     return PACT_OK;
