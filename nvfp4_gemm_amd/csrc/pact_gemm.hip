@@ -36,6 +36,17 @@
 
 namespace pact {
 
+struct DownArgs {
+    const uint16_t *X;  // nullptr: no fused LoRA-down
+    int64_t ldx;
+    int M, Kl;
+    const uint16_t *Ps;
+    int64_t p_sj, p_sk;
+    int r, rpad, j0;
+    float scale;
+    uint16_t *T;
+};
+
 struct GemmArgs {
     const uint8_t *a_codes;
     const uint8_t *a_scales;
@@ -54,6 +65,7 @@ struct GemmArgs {
     int64_t ldy;
     int ks;       // K ranges split across workgroups (blockIdx.y); 1: no split
     float *part;  // ks > 1: FP32 partial fragments [ks][ceil(M/32)][ceil(N/32)][1024]
+    DownArgs down;  // ks > 1 and down.X: the LoRA-down runs as workgroups blockIdx.y == 0
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -313,6 +325,134 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
     });
 }
 
+// ---- LoRA down-projection --------------------------------------------------
+// T [M][rpad] = bf16(s . (Xl [M][Kl] . P^T)), P(j, k) = Ps[j p_sj + k p_sk] for
+// j < r, zero for r <= j < rpad; FP32 accumulation on v_mfma_f32_16x16x32_bf16.
+// The LoRA scale s is applied before the BF16 rounding; for a power-of-two s
+// this equals s . bf16(X P^T) exactly, i.e. the scale applied after the
+// rank-r product.
+// A group of 16 rows is computed by NW wavefronts, each taking a slice of K
+// and all RG groups of 16 ranks from one pass over its slice of X (the BF16
+// activations are the kernel's HBM traffic); the NW partial tiles are summed
+// through LDS in a fixed order.  Ranks beyond 64 take further passes.
+
+// K32 chunks whose loads are in flight together (fewer with more rank groups:
+// a 1024-thread workgroup has 128 VGPRs per thread)
+template <int RG>
+constexpr int down_chunks() { return RG == 1 ? 8 : RG == 2 ? 6 : 4; }
+
+// LDS floats of the reduction buffer
+template <int RG, int NW>
+constexpr int down_red_floats() { return NW * 16 * (16 * RG + 1); }
+
+// Rows m0 .. m0+15 of T, ranks j0 .. j0 + 16 RG.  Every thread of the
+// workgroup (NW wavefronts) calls it; red holds down_red_floats<RG, NW>().
+template <int RG, int NW>
+__device__ __forceinline__ void lora_down_rows(const DownArgs &d, int m0, float *red) {
+    constexpr int RS = 16 * RG + 1;  // row stride of a partial tile
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int row = min(m0 + (lane & 15), d.M - 1);
+    const int kg = 8 * (lane >> 4);
+    const int ks = ((d.Kl + NW - 1) / NW + 31) / 32 * 32;
+    const int kb = w * ks, ke = min(d.Kl, kb + ks);
+    const uint16_t *xr = d.X + (int64_t)row * d.ldx;
+    float4_t acc[RG];
+#pragma unroll
+    for (int f = 0; f < RG; ++f) acc[f] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // U chunks of 32 K per iteration: all their loads are issued before the
+    // MFMAs, so the loop is not bound by one load latency per chunk
+    constexpr int U = down_chunks<RG>();
+    for (int k0 = kb; k0 < ke; k0 += 32 * U) {
+        u32x4 va[U], vb[U][RG];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 32 * u + kg;
+            va[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int f = 0; f < RG; ++f) vb[u][f] = u32x4{0u, 0u, 0u, 0u};
+            if (k < ke) {
+                va[u] = *reinterpret_cast<const u32x4 *>(xr + k);
+#pragma unroll
+                for (int f = 0; f < RG; ++f) {
+                    const int j = d.j0 + 16 * f + (lane & 15);
+                    if (j < d.r) {
+                        if (d.p_sk == 1) {
+                            vb[u][f] = *reinterpret_cast<const u32x4 *>(d.Ps + (int64_t)j * d.p_sj + k);
+                        } else {
+                            uint32_t t[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                t[e] = (uint32_t)d.Ps[(int64_t)j * d.p_sj + (int64_t)(k + 2 * e) * d.p_sk] |
+                                       ((uint32_t)d.Ps[(int64_t)j * d.p_sj + (int64_t)(k + 2 * e + 1) * d.p_sk] << 16);
+                            vb[u][f] = u32x4{t[0], t[1], t[2], t[3]};
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int f = 0; f < RG; ++f)
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[u]),
+                                                                 __builtin_bit_cast(bf16x8_t, vb[u][f]), acc[f], 0,
+                                                                 0, 0);
+    }
+#pragma unroll
+    for (int f = 0; f < RG; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(w * 16 + 4 * (lane >> 4) + e) * RS + 16 * f + (lane & 15)] = acc[f][e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * 16 * RG; i += 64 * NW) {
+        const int mi = i / (16 * RG), ji = i % (16 * RG);
+        float sum = 0.0f;
+        for (int q = 0; q < NW; ++q) sum += red[(q * 16 + mi) * RS + ji];
+        const float ts = d.scale * sum;
+        if (m0 + mi < d.M) d.T[(int64_t)(m0 + mi) * d.rpad + d.j0 + ji] = (uint16_t)f32_to_bf16_bits(ts);
+    }
+    __syncthreads();  // red is reused by the caller's next row group
+}
+
+// LoRA-down as workgroups of a split-K main kernel (which does not read T):
+// row groups blockIdx.x, blockIdx.x + gridDim.x, ...; ranks up to 64.
+template <int NW>
+__device__ __forceinline__ void lora_down_fused(const DownArgs &d, float *red) {
+    const int groups = (d.M + 15) / 16;
+    for (int g = blockIdx.x; g < groups; g += gridDim.x) {
+        switch (d.rpad >> 4) {
+            case 1: lora_down_rows<1, NW>(d, 16 * g, red); break;
+            case 2: lora_down_rows<2, NW>(d, 16 * g, red); break;
+            case 3: lora_down_rows<3, NW>(d, 16 * g, red); break;
+            default: lora_down_rows<4, NW>(d, 16 * g, red); break;
+        }
+    }
+}
+
+constexpr int kDownWaves = 16;
+
+template <int RG>
+__global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
+    __shared__ float red[down_red_floats<RG, kDownWaves>()];
+    lora_down_rows<RG, kDownWaves>(d, blockIdx.x * 16, red);
+}
+
+static pact_status launch_lora_down(DownArgs d, hipStream_t st) {
+    const dim3 grid((unsigned)((d.M + 15) / 16)), block(64 * kDownWaves);
+    for (int j0 = 0; j0 < d.rpad; j0 += 64) {
+        d.j0 = j0;
+        const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
+        switch (rg) {
+            case 1: hipLaunchKernelGGL(lora_down_kernel<1>, grid, block, 0, st, d); break;
+            case 2: hipLaunchKernelGGL(lora_down_kernel<2>, grid, block, 0, st, d); break;
+            case 3: hipLaunchKernelGGL(lora_down_kernel<3>, grid, block, 0, st, d); break;
+            default: hipLaunchKernelGGL(lora_down_kernel<4>, grid, block, 0, st, d); break;
+        }
+        PACT_TRY(launch_status());
+    }
+    return PACT_OK;
+}
+
 // Split-K: a workgroup stores its FP32 partial fragments instead of running
 // the epilogue; fragment (i, j) of split s is 1024 floats at
 // part + ((s FM + i) FN + j) 1024, element e of lane l at (e / 4) 256 + 4 l +
@@ -320,13 +460,13 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
 // the output are not stored.
 template <int F, typename AccFn>
 __device__ __forceinline__ void store_partials(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
-                                               const int (&nb)[F]) {
+                                               const int (&nb)[F], int split) {
     const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5;
     static_for<F>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const int fi = mb[i] >> 5, fj = nb[i] >> 5;
         if (fi < FM && fj < FN) {
-            float *dst = p.part + (((int64_t)blockIdx.y * FM + fi) * FN + fj) * 1024 + 4 * lane;
+            float *dst = p.part + (((int64_t)split * FM + fi) * FN + fj) * 1024 + 4 * lane;
             const float16_t &a = accf(ic);
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
@@ -339,9 +479,9 @@ __device__ __forceinline__ void store_partials(const GemmArgs &p, int lane, AccF
 // End of a main kernel: the epilogue, or (split K) the partial store.
 template <bool SPLIT, int F, int G, typename AccFn>
 __device__ __forceinline__ void finish_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
-                                             const int (&nb)[F], float *tile) {
+                                             const int (&nb)[F], float *tile, int split) {
     if constexpr (SPLIT)
-        store_partials<F>(p, lane, accf, mb, nb);
+        store_partials<F>(p, lane, accf, mb, nb, split);
     else
         epi_frags<F, G>(p, lane, accf, mb, nb, tile);
 }
@@ -407,10 +547,20 @@ template <int WM, int WN, int WK, bool KFULL, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     using SH = GemmShape<WM, WN, WK>;
     static_assert(SH::LDS_BYTES >= 4 * 4 * epi_tile_floats<4>(), "LDS holds the epilogue tiles");
+    static_assert(SH::LDS_BYTES >= 4 * down_red_floats<4, 4>(), "LDS holds the fused LoRA-down buffer");
     constexpr int G = SH::G, BM = SH::BM, BN = SH::BN, ROWS = SH::ROWS;
     constexpr int PCODE = SH::PCODE, STAGE = SH::STAGE, LPW = SH::LPW, NQC = SH::NQC;
     __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
 
+    // split K: workgroups blockIdx.y == 0 compute the LoRA-down product when
+    // it is fused into this launch (the split-K epilogue reads it)
+    if constexpr (SPLIT) {
+        if (p.down.X && blockIdx.y == 0) {
+            lora_down_fused<4>(p.down, reinterpret_cast<float *>(lds));
+            return;
+        }
+    }
+    const int split = SPLIT ? (int)blockIdx.y - (p.down.X ? 1 : 0) : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int h = lane >> 5;
@@ -428,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     // stages per group (the host makes it exact); workgroup blockIdx.y of a
     // split-K launch takes the y-th of ks equal ranges of stages
     const int S = ((K + kSK - 1) / kSK) / (WK * p.ks);
-    const int gs0 = ((int)blockIdx.y * WK + grp) * S;  // first global stage of this group
+    const int gs0 = (split * WK + grp) * S;  // first global stage of this group
     uint8_t *const glds = lds + grp * SH::GROUP_BYTES;
 
     // ---- per-wavefront load assignment: load q of a stage ----
@@ -661,7 +811,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         finish_frags<SPLIT, 16, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return acc[i >> 2][i & 3];
-        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>());
+        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>(), split);
     } else {
         // Partial tiles summed through LDS, one fragment column per round:
         // every wavefront writes its 4 fragments of the column to slot
@@ -703,7 +853,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         finish_frags<SPLIT, NF, 4>(p, lane, [&](auto ic) -> float16_t & {
             constexpr int i = decltype(ic)::value;
             return own[i >> 2][i & 3];
-        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>());
+        }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<4>(), split);
     }
 }
 
@@ -748,11 +898,19 @@ template <bool SPLIT>
 __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     using SH = Gemm8Shape;
     static_assert(SH::LDS_BYTES >= 8 * 4 * epi_tile_floats<2>(), "LDS holds the epilogue tiles");
+    static_assert(SH::LDS_BYTES >= 4 * down_red_floats<4, 8>(), "LDS holds the fused LoRA-down buffer");
     constexpr int STAGE = SH::STAGE, PCODE = SH::PCODE, FPH = SH::FPH, LPW = SH::LPW;
     __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS_BYTES];
     uint8_t *const ring = lds;
     uint8_t *const F0 = lds + SH::RING;
 
+    if constexpr (SPLIT) {
+        if (p.down.X && blockIdx.y == 0) {  // fused LoRA-down workgroups
+            lora_down_fused<8>(p.down, reinterpret_cast<float *>(lds));
+            return;
+        }
+    }
+    const int split = SPLIT ? (int)blockIdx.y - (p.down.X ? 1 : 0) : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -765,7 +923,7 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     const int K = p.K;
     const int nblk = K >> 4;
     const int S = (K / kSK) / p.ks;  // stages (K % 64 == 0 for this kernel; the host makes it exact)
-    const int s0 = (int)blockIdx.y * S;  // first stage of this workgroup's K range
+    const int s0 = split * S;  // first stage of this workgroup's K range
 
     // ---- stage loads: wavefront w issues code loads w (A rows 32w..) and
     // w + 8 (B rows), and scale load w (rows 64w.., A when w < 4) ----
@@ -922,7 +1080,7 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     finish_frags<SPLIT, 8, 2>(p, lane, [&](auto ic) -> float16_t & {
         constexpr int i = decltype(ic)::value;
         return acc[i >> 1][i & 1];
-    }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<2>());
+    }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<2>(), split);
 }
 
 // Split-K epilogue: wavefront w takes the two horizontally adjacent output
@@ -964,109 +1122,6 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
     const int mbs[2] = {32 * fi, 32 * fi}, nbs[2] = {32 * fj, 32 * fj + 32};
     epi_frags<2, 2>(p, lane, [&](auto ic) -> float16_t & { return acc[decltype(ic)::value]; }, mbs, nbs,
                     tiles[threadIdx.x >> 6]);
-}
-
-// ---- LoRA down-projection --------------------------------------------------
-// T [M][rpad] = bf16(s . (Xl [M][Kl] . P^T)), P(j, k) = Ps[j p_sj + k p_sk] for
-// j < r, zero for r <= j < rpad; FP32 accumulation on v_mfma_f32_16x16x32_bf16.
-// The LoRA scale s is applied before the BF16 rounding; for a power-of-two s
-// this equals s . bf16(X P^T) exactly, i.e. the scale applied after the
-// rank-r product.
-// One workgroup of 16 wavefronts per 16 rows: each wavefront takes a slice of
-// K and computes RG groups of 16 ranks from one pass over its slice of X (the
-// BF16 activations are the kernel's HBM traffic), and the 16 partial tiles
-// are summed through LDS in a fixed order.  Ranks beyond 16 RG take further
-// passes (r > 64 only).
-constexpr int kDownWaves = 16;
-// K32 chunks whose loads are in flight together (fewer with more rank groups:
-// a 1024-thread workgroup has 128 VGPRs per thread)
-template <int RG>
-constexpr int down_chunks() { return RG == 1 ? 8 : RG == 2 ? 6 : 4; }
-
-template <int RG>
-__global__ __launch_bounds__(1024) void lora_down_kernel(const uint16_t *X, int64_t ldx, int M, int Kl,
-                                                         const uint16_t *Ps, int64_t p_sj, int64_t p_sk,
-                                                         int r, int rpad, int j0, float scale, uint16_t *T) {
-    __shared__ float red[kDownWaves][16][16 * RG + 1];
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int m0 = blockIdx.x * 16;
-    const int row = min(m0 + (lane & 15), M - 1);
-    const int kg = 8 * (lane >> 4);
-    const int ks = ((Kl + kDownWaves - 1) / kDownWaves + 31) / 32 * 32;
-    const int kb = w * ks, ke = min(Kl, kb + ks);
-    const uint16_t *xr = X + (int64_t)row * ldx;
-    float4_t acc[RG];
-#pragma unroll
-    for (int f = 0; f < RG; ++f) acc[f] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // U chunks of 32 K per iteration: all their loads are issued before the
-    // MFMAs, so the loop is not bound by one load latency per chunk
-    constexpr int U = down_chunks<RG>();
-    for (int k0 = kb; k0 < ke; k0 += 32 * U) {
-        u32x4 va[U], vb[U][RG];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + 32 * u + kg;
-            va[u] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int f = 0; f < RG; ++f) vb[u][f] = u32x4{0u, 0u, 0u, 0u};
-            if (k < ke) {
-                va[u] = *reinterpret_cast<const u32x4 *>(xr + k);
-#pragma unroll
-                for (int f = 0; f < RG; ++f) {
-                    const int j = j0 + 16 * f + (lane & 15);
-                    if (j < r) {
-                        if (p_sk == 1) {
-                            vb[u][f] = *reinterpret_cast<const u32x4 *>(Ps + (int64_t)j * p_sj + k);
-                        } else {
-                            uint32_t t[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                t[e] = (uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e) * p_sk] |
-                                       ((uint32_t)Ps[(int64_t)j * p_sj + (int64_t)(k + 2 * e + 1) * p_sk] << 16);
-                            vb[u][f] = u32x4{t[0], t[1], t[2], t[3]};
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int f = 0; f < RG; ++f)
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va[u]),
-                                                                 __builtin_bit_cast(bf16x8_t, vb[u][f]), acc[f], 0,
-                                                                 0, 0);
-    }
-#pragma unroll
-    for (int f = 0; f < RG; ++f)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[w][4 * (lane >> 4) + e][16 * f + (lane & 15)] = acc[f][e];
-    __syncthreads();
-    for (int i = threadIdx.x; i < 16 * 16 * RG; i += 1024) {
-        const int mi = i / (16 * RG), ji = i % (16 * RG);
-        float sum = 0.0f;
-        for (int q = 0; q < kDownWaves; ++q) sum += red[q][mi][ji];
-        const float ts = scale * sum;
-        if (m0 + mi < M) T[(int64_t)(m0 + mi) * rpad + j0 + ji] = (uint16_t)f32_to_bf16_bits(ts);
-    }
-}
-
-static pact_status launch_lora_down(const uint16_t *X, int64_t ldx, int M, int Kl, const uint16_t *Ps,
-                                    int64_t p_sj, int64_t p_sk, int r, int rpad, float scale, uint16_t *T,
-                                    hipStream_t st) {
-    const dim3 grid((unsigned)((M + 15) / 16)), block(64 * kDownWaves);
-    for (int j0 = 0; j0 < rpad; j0 += 64) {
-        const int rg = (rpad - j0) / 16 < 4 ? (rpad - j0) / 16 : 4;
-        switch (rg) {
-            case 1: hipLaunchKernelGGL(lora_down_kernel<1>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
-            case 2: hipLaunchKernelGGL(lora_down_kernel<2>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
-            case 3: hipLaunchKernelGGL(lora_down_kernel<3>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
-            default: hipLaunchKernelGGL(lora_down_kernel<4>, grid, block, 0, st, X, ldx, M, Kl, Ps, p_sj, p_sk, r, rpad, j0, scale, T); break;
-        }
-        PACT_TRY(launch_status());
-    }
-    return PACT_OK;
 }
 
 // ---- launch plan ------------------------------------------------------------
@@ -1155,7 +1210,7 @@ template <int WM, int WN, int WK>
 static void launch_gemm_cfg(const GemmArgs &a, hipStream_t st) {
     using SH = GemmShape<WM, WN, WK>;
     const int tiles = ((a.M + SH::BM - 1) / SH::BM) * ((a.N + SH::BN - 1) / SH::BN);
-    const dim3 grid((unsigned)tiles, (unsigned)a.ks);
+    const dim3 grid((unsigned)tiles, (unsigned)(a.ks + (a.ks > 1 && a.down.X ? 1 : 0)));
     if (a.ks > 1)  // the plan splits K only when K % 64 == 0
         hipLaunchKernelGGL((gemm_kernel<WM, WN, WK, true, true>), grid, dim3(256), 0, st, a);
     else if (a.K % kSK == 0)
@@ -1168,7 +1223,7 @@ static pact_status launch_plan(const GemmArgs &a, int kernel, hipStream_t st) {
     switch (kernel) {
         case 0: {
             const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-            const dim3 grid((unsigned)tiles, (unsigned)a.ks);
+            const dim3 grid((unsigned)tiles, (unsigned)(a.ks + (a.ks > 1 && a.down.X ? 1 : 0)));
             if (a.ks > 1)
                 hipLaunchKernelGGL(gemm8_kernel<true>, grid, dim3(512), 0, st, a);
             else
@@ -1248,7 +1303,11 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     if (r > 0) {
         const int rpad = (int)round_up(r, 16);
         uint16_t *T = static_cast<uint16_t *>(ws);
-        PACT_TRY(launch_lora_down(Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, lora->scale, T, st));
+        DownArgs d = {Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, 0, lora->scale, T};
+        if (plan.ks > 1 && rpad <= 64)
+            a.down = d;  // computed by workgroups of the split-K main kernel
+        else
+            PACT_TRY(launch_lora_down(d, st));
         a.T = T;
         a.Qs = Qsrc;
         a.q_sn = q_sn;
