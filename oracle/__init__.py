@@ -79,6 +79,13 @@ def lib():
                      ctypes.c_float, P, P, I64, P]
         L.orc_gemm_fwd.argtypes = gemm_args
         L.orc_gemm_dgrad.argtypes = gemm_args
+        L.orc_dsilu.restype = ctypes.c_float
+        L.orc_dsilu.argtypes = [ctypes.c_uint16]
+        L.orc_dsilu_check_table.restype = ctypes.c_int
+        L.orc_silu_mul_bwd_quant.argtypes = [P, I64, I64, I64] + [P] * 6 + [P, P] + [P] * 6
+        L.orc_dot_bf16_f32.restype = ctypes.c_double
+        L.orc_dot_bf16_f32.argtypes = [P, P, I64]
+        L.orc_rmsnorm_bwd.argtypes = [P, I64, P, P, P, P, P, P, I64, I64, I64, P, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -279,3 +286,51 @@ def gemm_dgrad(dyq: NVFP4, dY, wbq: NVFP4, A=None, B=None, s=1.0, C=None, rows=N
     """dX = bf16(d_dy d_wb (dYq . Wb^T) + s (bf16(dY B)) A (+ C)) for the listed rows.
     dY [M,N] bf16, W_bwd [K,N], A [r,K], B [N,r], C [M,K] or None."""
     return _gemm(lib().orc_gemm_dgrad, dyq, dY, wbq, A, B, s, C, rows)
+
+
+# ---- nonlinear backward from the NVFP4 stash ------------------------------
+def dsilu_table() -> np.ndarray:
+    """d/dg (g sigma(g)) correctly rounded to binary32 for all 65536 BF16 bit
+    patterns (NaN at non-finite patterns)."""
+    L = lib()
+    if L.orc_dsilu_check_table() != 0:
+        raise RuntimeError("oracle dsilu table has inputs too close to a rounding boundary")
+    return np.array([L.orc_dsilu(b) for b in range(65536)], np.float32)
+
+
+def silu_mul_bwd_quant(dh: np.ndarray, gq: NVFP4, uq: NVFP4):
+    """Returns (dg bf16 bits, du bf16 bits, dgq, duq) from dh and the gate/up stash."""
+    dh = _c(dh, np.uint16)
+    rows, cols = dh.shape
+    assert (gq.rows, gq.cols) == (rows, cols) and (uq.rows, uq.cols) == (rows, cols)
+    dg = np.zeros((rows, cols), np.uint16)
+    du = np.zeros((rows, cols), np.uint16)
+    dgq, duq = NVFP4.empty(rows, cols), NVFP4.empty(rows, cols)
+    lib().orc_silu_mul_bwd_quant(
+        _p(dh), cols, rows, cols,
+        _p(_c(gq.codes, np.uint8)), _p(_c(gq.scales, np.uint8)), _p(_c(gq.d, np.float32)),
+        _p(_c(uq.codes, np.uint8)), _p(_c(uq.scales, np.uint8)), _p(_c(uq.d, np.float32)),
+        _p(dg), _p(du), _p(dgq.codes), _p(dgq.scales), _p(dgq.d), _p(duq.codes), _p(duq.scales),
+        _p(duq.d))
+    return dg, du, dgq, duq
+
+
+def dot_bf16_f32(a: np.ndarray, b: np.ndarray) -> float:
+    a = _c(a, np.uint16)
+    b = _c(b, np.float32)
+    assert a.size == b.size
+    return float(lib().orc_dot_bf16_f32(_p(a), _p(b), a.size))
+
+
+def rmsnorm_bwd(dy: np.ndarray, yq: NVFP4, gamma: np.ndarray, rstd: np.ndarray, C=None):
+    """Returns (dx bf16 bits, dxq) from dy, the NVFP4 norm output, gamma and rstd."""
+    dy = _c(dy, np.uint16)
+    rows, cols = dy.shape
+    assert (yq.rows, yq.cols) == (rows, cols)
+    dx = np.zeros((rows, cols), np.uint16)
+    dxq = NVFP4.empty(rows, cols)
+    Cc = _c(C, np.uint16) if C is not None else None
+    lib().orc_rmsnorm_bwd(_p(dy), cols, _p(_c(yq.codes, np.uint8)), _p(_c(yq.scales, np.uint8)),
+                          _p(_c(yq.d, np.float32)), _p(_c(gamma, np.uint16)), _p(_c(rstd, np.float32)),
+                          _p(Cc), cols, rows, cols, _p(dx), _p(dxq.codes), _p(dxq.scales), _p(dxq.d))
+    return dx, dxq

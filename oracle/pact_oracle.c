@@ -467,3 +467,225 @@ void orc_gemm_dgrad(const uint8_t *gc, const uint8_t *gs, const float *gd,
     /* T' = dY B: P[j,n] = B[n*r + j];  L' = T' A: Q[k,j] = A[j*K + k] */
     gemm_tn_rows(gc, gs, gd, N, wc, ws, wd, K, dY, N, B, 1, r, A, 1, K, r, s, C, row_idx, n_rows, dX);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Nonlinear backward from the NVFP4 stash ([blog] Method bullet 2: the       */
+/* quantized RMSNorm output is reused in backward instead of a separately     */
+/* saved norm input; the SiLU-multiply keeps an NVFP4 copy of gate/up for     */
+/* backward; [abstract]: quantized RMSNorm outputs reused, gate/up saved in   */
+/* NVFP4 for backward).                                                       */
+/* ------------------------------------------------------------------------- */
+
+/* d/dg of g*sigma(g) = sigma(g) (1 + g (1 - sigma(g))), correctly rounded to
+ * binary32 for a BF16 g, evaluated in binary128 like sigmoid_q (an input is
+ * flagged when its quad value lies within 2^-100 of a binary32 midpoint). */
+static float g_dsilu_table[65536];
+static int g_dsilu_unsafe = -1;
+
+static float dsilu_q(uint16_t gb, int *unsafe) {
+    __float128 g = (__float128)orc_bf16_to_f32(gb);
+    __float128 s = 1.0Q / (1.0Q + expq(-g));
+    __float128 v = s * (1.0Q + g * (1.0Q - s));
+    float r = (float)v;
+    *unsafe = 0;
+    if (v != 0.0Q && (__float128)r != v) {
+        float nb = ((__float128)r < v) ? nextafterf(r, INFINITY) : nextafterf(r, -INFINITY);
+        __float128 mid = ((__float128)r + (__float128)nb) / 2.0Q;
+        if (fabsq(v - mid) <= fabsq(v) * ldexpq(1.0Q, -100)) *unsafe = 1;
+    }
+    return r;
+}
+
+static void build_dsilu_table(void) {
+    int bad = 0;
+    for (uint32_t b = 0; b < 65536; ++b) {
+        if (((b >> 7) & 0xFF) == 0xFF) { g_dsilu_table[b] = NAN; continue; }
+        int u;
+        g_dsilu_table[b] = dsilu_q((uint16_t)b, &u);
+        bad += u;
+    }
+    g_dsilu_unsafe = bad;
+}
+
+int orc_dsilu_check_table(void) {
+    if (g_dsilu_unsafe < 0) build_dsilu_table();
+    return g_dsilu_unsafe;
+}
+
+float orc_dsilu(uint16_t g_bits) {
+    if (g_dsilu_unsafe < 0) build_dsilu_table();
+    return g_dsilu_table[g_bits];
+}
+
+/* Dequantized value of element k of an NVFP4 row: fl32((code value x block
+ * scale) x row scale), the product of the first two being exact. */
+static float deq_elem(const uint8_t *codes, const uint8_t *scales, float d, int64_t k) {
+    return operand_value(codes, scales, k) * d;
+}
+
+/* SiLU-multiply backward.  Readings: the stashed g and u are dequantized and
+ * taken in BF16 (g' = bf16(deq(gq)), u' = bf16(deq(uq)); the BF16 rounding is
+ * far below the NVFP4 error and makes silu and its derivative correctly
+ * rounded binary32 values of BF16 inputs); du = bf16(dh * sigma32(g')),
+ * dg = bf16((dh * u') * dsilu32(g')), each product one binary32 rounding;
+ * dgq = Q(dg), duq = Q(du) for the gate/up input-gradient GEMMs. */
+void orc_silu_mul_bwd_quant(const uint16_t *dh, int64_t ld, int64_t rows, int64_t cols,
+                            const uint8_t *gc, const uint8_t *gs, const float *gd,
+                            const uint8_t *uc, const uint8_t *us, const float *ud,
+                            uint16_t *dg, uint16_t *du,
+                            uint8_t *dgc, uint8_t *dgs, float *dgd,
+                            uint8_t *duc, uint8_t *dus, float *dud) {
+    assert(cols % 16 == 0);
+    if (g_sig_unsafe < 0) build_sig_table();
+    if (g_dsilu_unsafe < 0) build_dsilu_table();
+    assert(g_sig_unsafe == 0 && g_dsilu_unsafe == 0);
+#pragma omp parallel
+    {
+        float *grow = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+        float *urow = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const uint8_t *gci = gc + i * (cols / 2), *gsi = gs + i * (cols / 16);
+            const uint8_t *uci = uc + i * (cols / 2), *usi = us + i * (cols / 16);
+            for (int64_t j = 0; j < cols; ++j) {
+                uint16_t gb = orc_f32_to_bf16(deq_elem(gci, gsi, gd[i], j));
+                float up = orc_bf16_to_f32(orc_f32_to_bf16(deq_elem(uci, usi, ud[i], j)));
+                float d = orc_bf16_to_f32(dh[i * ld + j]);
+                uint16_t dub = orc_f32_to_bf16(d * g_sig_table[gb]);
+                float t = d * up;
+                uint16_t dgb = orc_f32_to_bf16(t * g_dsilu_table[gb]);
+                if (dg) dg[i * cols + j] = dgb;
+                if (du) du[i * cols + j] = dub;
+                grow[j] = orc_bf16_to_f32(dgb);
+                urow[j] = orc_bf16_to_f32(dub);
+            }
+            if (dgc) quantize_row(grow, cols, dgc + i * (cols / 2), dgs + i * (cols / 16), dgd + i);
+            if (duc) quantize_row(urow, cols, duc + i * (cols / 2), dus + i * (cols / 16), dud + i);
+        }
+        free(grow);
+        free(urow);
+    }
+}
+
+/* Exact dot product of a BF16 vector and a binary32 vector, rounded once to
+ * binary64.  A BF16 value is M1 2^k1 (M1 < 2^8, -133 <= k1 <= 120), a binary32
+ * value M2 2^k2 (M2 < 2^24, -149 <= k2 <= 104), so every product is an integer
+ * (< 2^32) times 2^-282 with exponent below 2^225; positive and negative
+ * products go to two 704-bit accumulators, subtracted at the end. */
+#define DOT_LIMBS 11
+static void acc_add(uint64_t *acc, uint64_t v, int pos) {
+    int limb = pos / 64, sh = pos % 64;
+    unsigned __int128 w = (unsigned __int128)v << sh;
+    uint64_t carry = 0;
+    for (int L = limb; L < DOT_LIMBS; ++L) {
+        unsigned __int128 add = (L == limb) ? (uint64_t)w : (L == limb + 1) ? (uint64_t)(w >> 64) : 0;
+        unsigned __int128 s = (unsigned __int128)acc[L] + add + carry;
+        acc[L] = (uint64_t)s;
+        carry = (uint64_t)(s >> 64);
+        if (L > limb + 1 && carry == 0) break;
+    }
+    assert(carry == 0);
+}
+
+static int acc_cmp(const uint64_t *a, const uint64_t *b) {
+    for (int L = DOT_LIMBS - 1; L >= 0; --L)
+        if (a[L] != b[L]) return a[L] > b[L] ? 1 : -1;
+    return 0;
+}
+
+static void acc_sub(uint64_t *a, const uint64_t *b) { /* a -= b, a >= b */
+    uint64_t borrow = 0;
+    for (int L = 0; L < DOT_LIMBS; ++L) {
+        unsigned __int128 s = (unsigned __int128)a[L] - b[L] - borrow;
+        a[L] = (uint64_t)s;
+        borrow = (uint64_t)(s >> 64) ? 1 : 0;
+    }
+}
+
+/* Round acc * 2^-unit_exp to nearest even binary64 (the values here stay far
+ * inside the binary64 range). */
+static double acc_round(const uint64_t *acc, int unit_exp) {
+    int top = -1;
+    for (int L = DOT_LIMBS - 1; L >= 0 && top < 0; --L)
+        if (acc[L]) top = L * 64 + 63 - __builtin_clzll(acc[L]);
+    if (top < 0) return 0.0;
+#define BIT(p) ((p) < 0 ? 0u : (unsigned)((acc[(p) / 64] >> ((p) % 64)) & 1u))
+    uint64_t mant = 0;
+    for (int p = top; p > top - 53; --p) mant = (mant << 1) | BIT(p);
+    int lsb = top - 52;
+    unsigned round_bit = BIT(lsb - 1);
+    unsigned sticky = 0;
+    for (int p = lsb - 2; p >= 0; --p) sticky |= BIT(p);
+#undef BIT
+    if (round_bit && (sticky || (mant & 1u))) mant += 1;
+    return ldexp((double)mant, lsb - unit_exp);
+}
+
+double orc_dot_bf16_f32(const uint16_t *a, const float *b, int64_t n) {
+    uint64_t pos[DOT_LIMBS], neg[DOT_LIMBS];
+    memset(pos, 0, sizeof pos);
+    memset(neg, 0, sizeof neg);
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t e1 = (a[i] >> 7) & 0xFF, f1 = a[i] & 0x7F;
+        assert(e1 != 0xFF);
+        uint64_t M1 = (e1 == 0) ? f1 : (128u + f1);
+        int k1 = (e1 == 0) ? -133 : (int)e1 - 127 - 7;
+        uint32_t bb;
+        memcpy(&bb, &b[i], 4);
+        uint32_t e2 = (bb >> 23) & 0xFF, f2 = bb & 0x7FFFFF;
+        assert(e2 != 0xFF);
+        uint64_t M2 = (e2 == 0) ? f2 : ((1u << 23) + f2);
+        int k2 = (e2 == 0) ? -149 : (int)e2 - 127 - 23;
+        if (M1 == 0 || M2 == 0) continue;
+        int neg_sign = ((a[i] >> 15) ^ (bb >> 31)) & 1;
+        acc_add(neg_sign ? neg : pos, M1 * M2, k1 + k2 + 282);
+    }
+    if (acc_cmp(pos, neg) >= 0) {
+        acc_sub(pos, neg);
+        return acc_round(pos, 282);
+    }
+    acc_sub(neg, pos);
+    return -acc_round(neg, 282);
+}
+
+/* RMSNorm backward from the stash.  With y = x rstd gamma and x^ = x rstd,
+ * dx = rstd (g - x^ mean(g x^)), g = dy gamma.  Readings: x^ is recovered
+ * from the NVFP4 stash as y'/gamma with y' = deq(yq) in binary32 (x^ = 0
+ * where gamma = 0); since g x^ = dy y', the mean is S/H with S the exact sum
+ * of dy y' rounded once to binary64, c = fl32(S / H) (binary64 division);
+ * per element dx = bf16(fl32(fl32(fl32(dy gamma) - fl32(x^ c)) rstd)
+ * (+ C, one more binary32 rounding before the BF16 one); optional dxq = Q(dx).
+ * gamma is frozen (no gamma gradient). */
+void orc_rmsnorm_bwd(const uint16_t *dy, int64_t ld, const uint8_t *yc, const uint8_t *ys,
+                     const float *yd, const uint16_t *gamma, const float *rstd, const uint16_t *C,
+                     int64_t ldc, int64_t rows, int64_t cols, uint16_t *dx, uint8_t *dxc,
+                     uint8_t *dxs, float *dxd) {
+    assert(cols % 16 == 0);
+#pragma omp parallel
+    {
+        float *yrow = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+        float *xrow = (float *)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const uint8_t *yci = yc + i * (cols / 2), *ysi = ys + i * (cols / 16);
+            for (int64_t j = 0; j < cols; ++j) yrow[j] = deq_elem(yci, ysi, yd[i], j);
+            const double S = orc_dot_bf16_f32(dy + i * ld, yrow, cols);
+            const float c = (float)(S / (double)cols);
+            const float r = rstd[i];
+            for (int64_t j = 0; j < cols; ++j) {
+                const float gm = orc_bf16_to_f32(gamma[j]);
+                const float xh = gm != 0.0f ? yrow[j] / gm : 0.0f;
+                const float g = orc_bf16_to_f32(dy[i * ld + j]) * gm;
+                const float t = xh * c;
+                const float v = (g - t) * r;
+                const float w = C ? v + orc_bf16_to_f32(C[i * ldc + j]) : v;
+                const uint16_t b = orc_f32_to_bf16(w);
+                if (dx) dx[i * cols + j] = b;
+                xrow[j] = orc_bf16_to_f32(b);
+            }
+            if (dxc) quantize_row(xrow, cols, dxc + i * (cols / 2), dxs + i * (cols / 16), dxd + i);
+        }
+        free(yrow);
+        free(xrow);
+    }
+}

@@ -96,6 +96,27 @@ void orc_gemm_dgrad(const uint8_t *gc, const uint8_t *gs, const float *gd,
                     const uint16_t *A, const uint16_t *B, int32_t r, float s,
                     const uint16_t *C, const int64_t *row_idx, int64_t n_rows, uint16_t *dX);
 
+/* ---- nonlinear backward from the NVFP4 stash ([blog] Method, bullet 2;
+ * [abstract]: quantized RMSNorm outputs reused, gate/up saved in NVFP4) ---- */
+float orc_dsilu(uint16_t g_bits);           /* correctly rounded binary32 of d/dg (g sigma(g)) */
+int   orc_dsilu_check_table(void);          /* 0 if every finite BF16 input was decided safely */
+/* g' = bf16(deq(gq)), u' = bf16(deq(uq)); du = bf16(dh sigma32(g')),
+ * dg = bf16((dh u') dsilu32(g')); dgq = Q(dg), duq = Q(du) (outputs may be NULL) */
+void  orc_silu_mul_bwd_quant(const uint16_t *dh, int64_t ld, int64_t rows, int64_t cols,
+                             const uint8_t *gc, const uint8_t *gs, const float *gd,
+                             const uint8_t *uc, const uint8_t *us, const float *ud,
+                             uint16_t *dg, uint16_t *du,
+                             uint8_t *dgc, uint8_t *dgs, float *dgd,
+                             uint8_t *duc, uint8_t *dus, float *dud);
+/* exact dot product of a BF16 and a binary32 vector, rounded once to binary64 */
+double orc_dot_bf16_f32(const uint16_t *a, const float *b, int64_t n);
+/* dx = bf16(((dy gamma) - x^ c) rstd (+ C)), x^ = deq(yq)/gamma, c = fl32(S/H),
+ * S = exact sum of dy deq(yq); dxq = Q(dx) (dx, dxq, C may be NULL) */
+void  orc_rmsnorm_bwd(const uint16_t *dy, int64_t ld, const uint8_t *yc, const uint8_t *ys,
+                      const float *yd, const uint16_t *gamma, const float *rstd,
+                      const uint16_t *C, int64_t ldc, int64_t rows, int64_t cols, uint16_t *dx,
+                      uint8_t *dxc, uint8_t *dxs, float *dxd);
+
 int orc_num_threads(void);
 
 #ifdef __cplusplus
