@@ -11,13 +11,19 @@ One step of a layer (every call goes through the C ABI):
             stand-in), aq = Q(a), x2 = fwd_o(aq, a, C = x)
             n2, n2q, rstd2 = rmsnorm_quant(x2); g, u = fwd GEMMs on n2q
             h, hq, gq, uq = silu_mul_quant(g, u); x' = fwd_down(hq, h, C = x2)
-  backward: dh = dgrad_down(Q(dx'), dx'); stand-in dg = du = dh
-            dx2 = dgrad_up(Q(dh), dh, C = dgrad_gate(Q(dh), dh, C = dx'))
-            da = dgrad_o(Q(dx2), dx2); stand-ins dq = da, dk = da[:, :KV],
-            dv = da[:, KV:2KV]
-            dx = dgrad_v(Q(dv), dv, C = dgrad_k(Q(dk), dk, C = dgrad_q(Q(dq), dq, C = dx2)))
+  backward: dh = dgrad_down(Q(dx'), dx')
+            dg, du, dgq, duq = silu_mul_bwd(dh, gq, uq)          (from the stash)
+            dn2 = dgrad_up(duq, du, C = dgrad_gate(dgq, dg))
+            dx2, dx2q = rmsnorm_bwd(dn2, n2q, gamma2, rstd2, C = dx')   (residual)
+            da = dgrad_o(dx2q, dx2); attention backward stand-ins dq = da,
+            dk = da[:, :KV], dv = da[:, KV:2KV]
+            dn1 = dgrad_v(Q(dv), dv, C = dgrad_k(Q(dk), dk, C = dgrad_q(Q(dq), dq)))
+            dx, Q(dx) = rmsnorm_bwd(dn1, n1q, gamma1, rstd1, C = dx2)
+            (Q(dx) is the next layer's Q(dx'); Q(dx') is a separate call only
+            for the last layer)
 A stack runs the layers' forwards in order, keeping each layer's NVFP4 stash
-(n1q, aq, n2q, gq, uq, hq, rstd1, rstd2), then the backwards in reverse order.
+(n1q, aq, n2q, gq, uq, hq, rstd1, rstd2), then the backwards in reverse order;
+the backward consumes n1q, n2q, gq, uq and the rstd rows.
 The single-linear workload is Q(X), fwd, Q(dY), dgrad.  Weights and both
 cached NVFP4 layouts are built once before timing.
 
@@ -138,7 +144,9 @@ class Stack:
         self.n1, self.q, self.k, self.v = E(M, H), E(M, H), E(M, KV), E(M, KV)
         self.x2, self.n2 = E(M, H), E(M, H)
         self.gt, self.up, self.h = E(M, I), E(M, I), E(M, I)
-        self.doq, self.dh, self.dhq = Q(M, H), E(M, I), Q(M, I)
+        self.doq, self.dh = Q(M, H), E(M, I)
+        self.dg, self.du, self.dgq, self.duq = E(M, I), E(M, I), Q(M, I), Q(M, I)
+        self.dn = E(M, H)                        # gradient of a norm output (n2, then n1)
         self.dx2, self.dx2q, self.da = E(M, H), Q(M, H), E(M, H)
         self.dqq, self.dkq, self.dvq = Q(M, H), Q(M, KV), Q(M, KV)
         self.dxs = [self.dout, E(M, H), E(M, H)]
@@ -184,31 +192,42 @@ class Stack:
                 st["hq"], Wf["down"], X=self.h, lora=L["down"], C=self.x2, Y=xo, ws=ws), lora_fl(H, I)))
         # backward (input gradients), last layer first
         for j, l in enumerate(reversed(range(self.L))):
-            L, Wb = self.lora[l], self.Wb[l]
+            st, L, Wb = self.stash[l], self.lora[l], self.Wb[l]
             dout = self.dxs[0] if j == 0 else self.dxs[1 + (j - 1) % 2]
             dx = self.dxs[1 + j % 2]
-            c.append(("quantize", 0, M * H * 2 + nvb(M, H),
-                      lambda dout=dout: pb.pact_quantize_nvfp4(dout, self.doq), 0))
+            if j == 0:  # later layers get Q(dout) from the RMSNorm backward above them
+                c.append(("quantize", 0, M * H * 2 + nvb(M, H),
+                          lambda dout=dout: pb.pact_quantize_nvfp4(dout, self.doq), 0))
             c.append(("gemm_dgrad", gemm_fl(H, I), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.doq, Wb["down"], dY=dout, lora=L["down"], dX=self.dh, ws=ws), lora_fl(H, I)))
-            c.append(("quantize", 0, M * I * 2 + nvb(M, I), lambda: pb.pact_quantize_nvfp4(self.dh, self.dhq), 0))
-            c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
-                self.dhq, Wb["gate"], dY=self.dh, lora=L["gate"], C=dout, dX=self.dx2, ws=ws), lora_fl(I, H)))
+            c.append(("silu_mul_bwd", 0, M * I * 2 + 2 * nvb(M, I) + 2 * M * I * 2 + 2 * nvb(M, I),
+                      lambda st=st: pb.pact_silu_mul_bwd_quant_nvfp4(self.dh, st["gq"], st["uq"], self.dg, self.du,
+                                                                     self.dgq, self.duq), 0))
             c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
-                self.dhq, Wb["up"], dY=self.dh, lora=L["up"], C=self.dx2, dX=self.dx2, ws=ws), lora_fl(I, H)))
-            c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda: pb.pact_quantize_nvfp4(self.dx2, self.dx2q), 0))
+                self.dgq, Wb["gate"], dY=self.dg, lora=L["gate"], dX=self.dn, ws=ws), lora_fl(I, H)))
+            c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.duq, Wb["up"], dY=self.du, lora=L["up"], C=self.dn, dX=self.dn, ws=ws), lora_fl(I, H)))
+            c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2 + nvb(M, H),
+                      lambda st=st, l=l, dout=dout: pb.pact_rmsnorm_bwd_nvfp4(
+                          self.dn, st["n2q"], self.g2[l], st["rstd2"], C=dout, dx=self.dx2, dxq=self.dx2q), 0))
             c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dx2q, Wb["o"], dY=self.dx2, lora=L["o"], dX=self.da, ws=ws), lora_fl(H, H)))
             dq, dk, dv = self.da, self.da[:, :KV], self.da[:, KV:2 * KV]
             c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda dq=dq: pb.pact_quantize_nvfp4(dq, self.dqq), 0))
             c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dk=dk: pb.pact_quantize_nvfp4(dk, self.dkq), 0))
             c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dv=dv: pb.pact_quantize_nvfp4(dv, self.dvq), 0))
-            c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda dq=dq, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
-                self.dqq, Wb["q"], dY=dq, lora=L["q"], C=self.dx2, dX=dx, ws=ws), lora_fl(H, H)))
-            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dk=dk, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
-                self.dkq, Wb["k"], dY=dk, lora=L["k"], C=dx, dX=dx, ws=ws), lora_fl(KV, H)))
-            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, dx=dx, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
-                self.dvq, Wb["v"], dY=dv, lora=L["v"], C=dx, dX=dx, ws=ws), lora_fl(KV, H)))
+            c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda dq=dq, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dqq, Wb["q"], dY=dq, lora=L["q"], dX=self.dn, ws=ws), lora_fl(H, H)))
+            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dk=dk, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dkq, Wb["k"], dY=dk, lora=L["k"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
+            c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
+                self.dvq, Wb["v"], dY=dv, lora=L["v"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
+            last = j == self.L - 1
+            c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2
+                      + (0 if last else nvb(M, H)),
+                      lambda st=st, l=l, dx=dx, last=last: pb.pact_rmsnorm_bwd_nvfp4(
+                          self.dn, st["n1q"], self.g1[l], st["rstd1"], C=self.dx2, dx=dx,
+                          dxq=None if last else self.doq, want_q=not last), 0))
         return c
 
     def stash_bytes(self):
@@ -352,7 +371,7 @@ def isolated_timing(torch, calls, reps=10):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream()
     out = {}
-    for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant"):
+    for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant", "silu_mul_bwd", "rmsnorm_bwd"):
         cs = [c for c in calls if c[0] == kind]
         if not cs:
             continue

@@ -181,10 +181,45 @@ pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16_t *dY, int
                                   const uint16_t *C, uint16_t *dX, int64_t ld_dx,
                                   void *ws, size_t ws_bytes, void *stream);
 
+/* SiLU*mul backward from the NVFP4 gate/up stash (blog "Method", second
+ * bullet: gate/up are kept in NVFP4 for backward; abstract: "saves gate/up
+ * activations in NVFP4 for backward"):
+ *   g' = bf16(deq(gq)), u' = bf16(deq(uq))   (deq: code x block scale x row scale),
+ *   du = bf16(fl32(dh sigma32(g'))),  dg = bf16(fl32(fl32(dh u') dsilu32(g'))),
+ *   dgq = Q(dg), duq = Q(du)   (the operands of the gate/up input-gradient GEMMs),
+ * with sigma32 as in the forward and dsilu32(g) the correctly rounded binary32
+ * value of sigma(g) (1 + g (1 - sigma(g))).  dh [rows][cols] BF16 (ld_dh); gq,
+ * uq the forward's stash; dg, du [rows][cols] BF16 with leading dimension
+ * ld_out (each may be NULL); dgq, duq required.  cols % 16 == 0. */
+pact_status pact_silu_mul_bwd_quant_nvfp4(const uint16_t *dh, int64_t ld_dh, const pact_nvfp4 *gq,
+                                          const pact_nvfp4 *uq, int64_t rows, int64_t cols,
+                                          uint16_t *dg, uint16_t *du, int64_t ld_out,
+                                          const pact_nvfp4 *dgq, const pact_nvfp4 *duq, void *stream);
+
+/* RMSNorm backward from the NVFP4 norm output (blog "Method", second bullet:
+ * the quantized RMSNorm output is reused in backward, the norm input is not
+ * saved).  With x^ = y'/gamma, y' = deq(yq) (x^ = 0 where gamma = 0), and
+ * S = sum_j dy_j y'_j summed exactly (to 2^-106 relative) and rounded once,
+ * c = fl32(S / cols):
+ *   dx = bf16( fl32( fl32(dy gamma) - fl32(x^ c) ) rstd  (+ C) ),  dxq = Q(dx),
+ * the input gradient of y = x rstd gamma (gamma is frozen: no gamma gradient).
+ * dy [rows][cols] BF16 (ld_dy); yq and rstd [rows] from
+ * pact_rmsnorm_quant_nvfp4; gamma [cols]; C [rows][cols] (ld_c; the residual
+ * gradient, may be NULL); dx [rows][cols] (ld_dx; may be NULL) and dxq (may be
+ * NULL), not both NULL.  cols % 16 == 0. */
+pact_status pact_rmsnorm_bwd_nvfp4(const uint16_t *dy, int64_t ld_dy, const pact_nvfp4 *yq,
+                                   const uint16_t *gamma, const float *rstd, const uint16_t *C,
+                                   int64_t ld_c, int64_t rows, int64_t cols, uint16_t *dx,
+                                   int64_t ld_dx, const pact_nvfp4 *dxq, void *stream);
+
 /* Diagnostic: out[i] = sigma32(g[i]) (the binary32 sigmoid-times-input the
  * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
  * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */
 pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64_t n, void *stream);
+
+/* Diagnostic: out[i] = dsilu32(g[i]) (the binary32 SiLU derivative the SiLU
+ * backward uses) for n BF16 inputs g.  Device pointers; stream-ordered. */
+pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *stream);
 
 /* Diagnostic: the launch plan of a GEMM with output [M][N] contracted over K
  * on the current device (host only, no GPU work): *kernel = 0 for the

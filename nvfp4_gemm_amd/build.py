@@ -39,14 +39,15 @@ def _compile(src: str) -> str:
 
 
 def _sigmoid_table() -> None:
-    """Generates the SiLU kernel's sigma32 table (a host program run at build time)."""
+    """Generates the SiLU kernels' sigma32 and dsilu32 tables (a host program run at build time)."""
     exe = os.path.join(BUILD, "gen_sigmoid_table")
     cmd = [os.environ.get("CXX", "g++"), "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
            os.path.join(CSRC, "gen_sigmoid_table.cpp"), "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"table generator build failed:\n{r.stderr}")
-    r = subprocess.run([exe, os.path.join(BUILD, "pact_sigmoid_table.inc")], capture_output=True, text=True)
+    r = subprocess.run([exe, os.path.join(BUILD, "pact_sigmoid_table.inc"),
+                        os.path.join(BUILD, "pact_dsilu_table.inc")], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"table generator failed:\n{r.stderr}")
 

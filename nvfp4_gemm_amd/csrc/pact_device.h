@@ -78,6 +78,37 @@ __device__ __forceinline__ float quot_f32(float x, float S) {
     return (float)((double)x / (double)S);
 }
 
+// Packed FP4 dword (8 codes, element 2j in the low nibble of byte j) -> 8
+// FP16 values scaled by the block scale sc: the E2M1 x E4M3 products are
+// exact in FP16 (at most 6 significant bits, magnitudes in [2^-10, 2688]).
+__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t sc) {
+    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, h0);
+    r.y = __builtin_bit_cast(uint32_t, h1);
+    r.z = __builtin_bit_cast(uint32_t, h2);
+    r.w = __builtin_bit_cast(uint32_t, h3);
+    return __builtin_bit_cast(half8_t, r);
+}
+
+// Dequantized values of one NVFP4 block: R[j] = fl32(code_j x scale) x d,
+// the first product exact (FP16), one binary32 rounding by the row scale d.
+__device__ __forceinline__ void dequant16(uint32_t c0, uint32_t c1, uint32_t scale_byte, float d, float R[16]) {
+    const half2_t sh = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)scale_byte, 1.0f, false);
+    half2_t sc;
+    sc[0] = sh[0];
+    sc[1] = sh[0];
+    const half8_t h0 = decode8(c0, sc), h1 = decode8(c1, sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        R[j] = (float)h0[j] * d;
+        R[8 + j] = (float)h1[j] * d;
+    }
+}
+
 // Per-row parameters of the quantizer.
 struct RowQ {
     float d;    // row scale

@@ -87,20 +87,6 @@ __device__ __forceinline__ void lds_barrier() {
 // loads of a stage, have completed.
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Packed FP4 dword (8 codes) -> 8 FP16 values (exact E2M1 x E4M3 products).
-__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t sc) {
-    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
-    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
-    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
-    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
-    u32x4 r;
-    r.x = __builtin_bit_cast(uint32_t, h0);
-    r.y = __builtin_bit_cast(uint32_t, h1);
-    r.z = __builtin_bit_cast(uint32_t, h2);
-    r.w = __builtin_bit_cast(uint32_t, h3);
-    return __builtin_bit_cast(half8_t, r);
-}
-
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
 // 8 XCDs (each with its own L2), so consecutive tiles of the launch order are
 // given to the same XCD; within an XCD's range, tiles run in groups of 4

@@ -27,7 +27,13 @@ struct NV {
     float *d;
 };
 
-enum { MODE_QUANT = 0, MODE_RMS = 1, MODE_SILU = 2 };
+enum { MODE_QUANT = 0, MODE_RMS = 1, MODE_SILU = 2, MODE_SILU_BWD = 3, MODE_RMS_BWD = 4 };
+
+struct CNV {  // NVFP4 input
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *d;
+};
 
 struct RowArgs {
     const uint16_t *x;  // QUANT/RMS: x, SILU: g
@@ -56,6 +62,19 @@ constexpr int kSigTab = 8192;
 __device__ const uint32_t kSigmoidCompact[kSigTab] = {
 #include "pact_sigmoid_table.inc"
 };
+
+// dsilu32(g): the correctly rounded binary32 value of d/dg (g / (1 + exp(-g)))
+// = sigma(g) (1 + g (1 - sigma(g))), same index and range as kSigmoidCompact;
+// outside it 0.5 below, 1 or -0 above by sign, 0 for Inf/NaN (same generator).
+__device__ const uint32_t kDsiluCompact[kSigTab] = {
+#include "pact_dsilu_table.inc"
+};
+
+__device__ __forceinline__ void load_dsilu_table(uint32_t *tab, int tid, int nthreads) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(kDsiluCompact);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(tab);
+    for (int i = tid; i < kSigTab / 4; i += nthreads) dst[i] = src[i];
+}
 
 __device__ __forceinline__ void load_sigmoid_table(uint32_t *tab, int tid, int nthreads) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(kSigmoidCompact);
@@ -108,6 +127,14 @@ __device__ __forceinline__ void silu32_x16(const uint32_t w[8], const uint32_t *
             s[2 * j + 1] = silu32_select(w[j] >> 16, t[2 * j + 1]);
         }
     }
+}
+
+// dsilu32 of a BF16 pattern b given its (always in-range) table entry t.
+__device__ __forceinline__ float dsilu32_select(uint32_t b, uint32_t t) {
+    const uint32_t e = (b >> 7) & 0xFFu;
+    const float big = (b & 0x8000u) ? -0.0f : 1.0f;
+    const float hi = e == 255u ? 0.0f : big;
+    return e < 102u ? 0.5f : (e < 134u ? __uint_as_float(t) : hi);
 }
 
 // Workgroup barrier ordering LDS only.
@@ -431,6 +458,307 @@ static pact_status launch_rows(const RowArgs &a, hipStream_t st) {
     return PACT_ERR_UNSUPPORTED_SHAPE;
 }
 
+// ---- nonlinear backward from the NVFP4 stash --------------------------------
+// (simolm.com PACT blog, section "Method", second bullet: the quantized RMSNorm
+// output is reused in backward instead of a saved norm input; the SiLU-multiply
+// keeps an NVFP4 copy of gate/up for backward.)
+//   SILU_BWD: g' = bf16(deq(gq)), u' = bf16(deq(uq)); du = bf16(dh sigma32(g')),
+//             dg = bf16((dh u') dsilu32(g')); dgq = Q(dg), duq = Q(du).
+//   RMS_BWD:  y' = deq(yq); S = sum dy y' (double-double, exact to 2^-106
+//             relative, rounded once); c = fl32(S / H); x^ = y'/gamma (0 where
+//             gamma = 0); dx = bf16(fl32(fl32(dy gamma) - fl32(x^ c)) rstd (+ C));
+//             dxq = Q(dx).
+// Same layout as the forward row kernels: one row per 64 WPR threads, each
+// thread owns whole 16-element blocks; NVFP4 blocks are read as 8 code bytes,
+// one scale byte and the row scale.
+struct BwdArgs {
+    const uint16_t *dy;  // SILU_BWD: dh, RMS_BWD: dy
+    int64_t lddy;
+    CNV in0;  // SILU_BWD: gq, RMS_BWD: yq
+    CNV in1;  // SILU_BWD: uq
+    const uint16_t *gamma;  // RMS_BWD
+    const float *rstd;      // RMS_BWD
+    const uint16_t *C;      // RMS_BWD residual (nullable)
+    int64_t ldc;
+    uint16_t *o0;  // SILU_BWD: dg, RMS_BWD: dx (nullable)
+    uint16_t *o1;  // SILU_BWD: du (nullable)
+    int64_t ldo;
+    NV q0;  // SILU_BWD: dgq, RMS_BWD: dxq (codes == nullptr: skip)
+    NV q1;  // SILU_BWD: duq
+    int64_t rows;
+    int cols;
+};
+
+__device__ __forceinline__ void load_codes(const CNV &q, int64_t row, int cols, int b, uint32_t &c0, uint32_t &c1,
+                                           uint32_t &sb) {
+    const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q.codes + row * (cols / 2) + 8 * b));
+    c0 = c.x;
+    c1 = c.y;
+    sb = __builtin_nontemporal_load(q.scales + row * (cols / 16) + b);
+}
+
+__device__ __forceinline__ void pack16(const float v[16], uint32_t w[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = f32x2_to_bf16x2(v[2 * j], v[2 * j + 1]);
+}
+
+template <int WPR, int BPL, int MODE>
+__global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
+    constexpr int NT = row_threads<WPR>();
+    constexpr int T = 64 * WPR;
+    constexpr int RPW = NT / T;
+    __shared__ float red[NT / 64][4];
+    __shared__ double redd[NT / 64][2];
+    __shared__ uint32_t tabs[MODE == MODE_SILU_BWD ? 2 * kSigTab : 1];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lrow = tid / T;
+    const int lt = tid % T;
+    const int cols = a.cols;
+    const int nb = cols >> 4;
+    if constexpr (MODE == MODE_SILU_BWD) {
+        load_sigmoid_table(tabs, tid, NT);
+        load_dsilu_table(tabs + kSigTab, tid, NT);
+        lds_sync();
+    }
+    const int64_t ngroups = (a.rows + RPW - 1) / RPW;
+    const int rl = __builtin_amdgcn_readfirstlane(lrow);
+    for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+        const int64_t row = grp * RPW + rl;
+        const bool active = row < a.rows;
+        const uint16_t *dyr = a.dy + row * a.lddy;
+        uint32_t dw[BPL][8];
+        uint32_t c0[BPL][2], s0[BPL];
+        uint32_t c1[MODE == MODE_SILU_BWD ? BPL : 1][2], s1[MODE == MODE_SILU_BWD ? BPL : 1];
+        uint32_t cw[MODE == MODE_RMS_BWD ? BPL : 1][8];
+        bool valid[BPL];
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int b = lt + T * i;
+            valid[i] = active && b < nb;
+            if (valid[i]) {
+                load_block(dyr, 32u * (uint32_t)b, dw[i]);
+                load_codes(a.in0, row, cols, b, c0[i][0], c0[i][1], s0[i]);
+                if constexpr (MODE == MODE_SILU_BWD) load_codes(a.in1, row, cols, b, c1[i][0], c1[i][1], s1[i]);
+                if constexpr (MODE == MODE_RMS_BWD) {
+                    if (a.C) load_block(a.C + row * a.ldc, 32u * (uint32_t)b, cw[i]);
+                }
+            }
+        }
+        const float d0 = active ? a.in0.d[row] : 0.0f;
+
+        if constexpr (MODE == MODE_SILU_BWD) {
+            const float d1 = active ? a.in1.d[row] : 0.0f;
+            float gmax[BPL], umax[BPL];
+            float rg = 0.0f, ru = 0.0f;
+            uint32_t gw[BPL][8], uw[BPL][8];  // dg, du as packed BF16
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                gmax[i] = umax[i] = 0.0f;
+                if (!valid[i]) continue;
+                float R[16];
+                uint32_t gb[8];
+                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                pack16(R, gb);  // g' as BF16
+                float U[16];
+                dequant16(c1[i][0], c1[i][1], s1[i], d1, U);
+                uint32_t ub[8];
+                pack16(U, ub);  // u' as BF16
+                // table reads for all 16 elements first, then the selection
+                uint32_t ts[16], td[16];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = silu32_index(gb[j] & 0xFFFFu), hi = silu32_index(gb[j] >> 16);
+                    ts[2 * j] = tabs[lo];
+                    ts[2 * j + 1] = tabs[hi];
+                    td[2 * j] = tabs[kSigTab + lo];
+                    td[2 * j + 1] = tabs[kSigTab + hi];
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(ts[j]), "+v"(td[j]));
+                float vg[16], vu[16];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t g16 = h ? (gb[j] >> 16) : (gb[j] & 0xFFFFu);
+                        const float sl = silu32_select(g16, ts[2 * j + h]);
+                        const float ds = dsilu32_select(g16, td[2 * j + h]);
+                        const float d = h ? bf16_hi(dw[i][j]) : bf16_lo(dw[i][j]);
+                        const float up = h ? bf16_hi(ub[j]) : bf16_lo(ub[j]);
+                        vu[2 * j + h] = d * sl;
+                        const float t = d * up;
+                        vg[2 * j + h] = t * ds;
+                    }
+                }
+                pack16(vg, gw[i]);
+                pack16(vu, uw[i]);
+                const int b = lt + T * i;
+                if (a.o0) store_block(a.o0 + row * a.ldo, 32u * (uint32_t)b, gw[i]);
+                if (a.o1) store_block(a.o1 + row * a.ldo, 32u * (uint32_t)b, uw[i]);
+                gmax[i] = amax16_packed(gw[i]);
+                umax[i] = amax16_packed(uw[i]);
+                rg = fmaxf(rg, gmax[i]);
+                ru = fmaxf(ru, umax[i]);
+            }
+            float dummy = 0.0f;
+            row_max3<WPR>(rg, ru, dummy, red, wave, lrow);
+            const RowQ qg = row_params(rg), qu = row_params(ru);
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                if (!valid[i]) continue;
+                const int b = lt + T * i;
+                float v[16];
+                opaque8(gw[i]);
+                opaque8(uw[i]);
+                if (a.q0.codes) {
+                    unpack16(gw[i], v);
+                    emit_block(a.q0, row, cols, b, v, gmax[i], qg);
+                }
+                if (a.q1.codes) {
+                    unpack16(uw[i], v);
+                    emit_block(a.q1, row, cols, b, v, umax[i], qu);
+                }
+            }
+            if (active && lt == 0) {
+                if (a.q0.codes) a.q0.d[row] = qg.d;
+                if (a.q1.codes) a.q1.d[row] = qu.d;
+            }
+        } else {  // MODE_RMS_BWD
+            // S = sum dy y': products are exact in binary64 (8 x 24 bits)
+            double s = 0.0, c = 0.0;
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                if (!valid[i]) continue;
+                float R[16], v[16];
+                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                unpack16(dw[i], v);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) dd_add(s, c, (double)v[j] * (double)R[j]);
+            }
+            wave_sum_dd(s, c);
+            s = __shfl(s, 0, 64);
+            c = __shfl(c, 0, 64);
+            if constexpr (WPR > 1) {
+                if ((tid & 63) == 0) {
+                    redd[wave][0] = s;
+                    redd[wave][1] = c;
+                }
+                lds_sync();
+                const int w0 = lrow * WPR;
+                s = redd[w0][0];
+                c = redd[w0][1];
+#pragma unroll
+                for (int w = 1; w < WPR; ++w) dd_add_dd(s, c, redd[w0 + w][0], redd[w0 + w][1]);
+                lds_sync();
+            }
+            const double S = s + c;
+            const float cm = (float)(S / (double)cols);
+            const float r = active ? a.rstd[row] : 0.0f;
+            float xmax[BPL];
+            float rx = 0.0f;
+            uint32_t xw[BPL][8];
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                xmax[i] = 0.0f;
+                if (!valid[i]) continue;
+                const int b = lt + T * i;
+                uint32_t gmw[8];
+                load_block_cached(a.gamma, 32u * (uint32_t)b, gmw);
+                float R[16], v[16], gm[16], o[16];
+                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                unpack16(dw[i], v);
+                unpack16(gmw, gm);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float xh = gm[j] != 0.0f ? R[j] / gm[j] : 0.0f;
+                    const float g = v[j] * gm[j];
+                    const float t = xh * cm;
+                    o[j] = (g - t) * r;
+                }
+                if (a.C) {
+                    float cv[16];
+                    unpack16(cw[i], cv);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[j] = o[j] + cv[j];
+                }
+                pack16(o, xw[i]);
+                if (a.o0) store_block(a.o0 + row * a.ldo, 32u * (uint32_t)b, xw[i]);
+                xmax[i] = amax16_packed(xw[i]);
+                rx = fmaxf(rx, xmax[i]);
+            }
+            if (a.q0.codes) {
+                float dummy1 = 0.0f, dummy2 = 0.0f;
+                row_max3<WPR>(rx, dummy1, dummy2, red, wave, lrow);
+                const RowQ rq = row_params(rx);
+#pragma unroll
+                for (int i = 0; i < BPL; ++i) {
+                    if (!valid[i]) continue;
+                    float v[16];
+                    opaque8(xw[i]);
+                    unpack16(xw[i], v);
+                    emit_block(a.q0, row, cols, lt + T * i, v, xmax[i], rq);
+                }
+                if (active && lt == 0) a.q0.d[row] = rq.d;
+            }
+        }
+        if constexpr (MODE != MODE_SILU_BWD) break;
+    }  // row groups
+}
+
+template <int MODE>
+static pact_status launch_bwd(const BwdArgs &a, hipStream_t st) {
+    if (a.rows == 0 || a.cols == 0) return PACT_OK;
+    const int nb = a.cols / 16;
+    int wpr, bpl;
+    if (nb <= 64) wpr = 1, bpl = 1;
+    else if (nb <= 128) wpr = 1, bpl = 2;
+    else if (nb <= 192) wpr = 1, bpl = 3;
+    else if (nb <= 256) wpr = 4, bpl = 1;
+    else if (nb <= 512) wpr = 8, bpl = 1;
+    else if (nb <= 1024) wpr = 8, bpl = 2;
+    else if (nb <= 1536) wpr = 8, bpl = 3;
+    else wpr = 8, bpl = 4;
+    const int threads = wpr > 4 ? 64 * wpr : 256;
+    const int rpw = threads / (64 * wpr);
+    const int64_t groups = (a.rows + rpw - 1) / rpw;
+    // SiLU backward: the two 32 KB tables allow two resident workgroups per CU
+    const int64_t cap = MODE == MODE_SILU_BWD ? (int64_t)device_cus() * 2 : groups;
+    const dim3 grid((unsigned)(groups < cap ? groups : cap));
+#define PACT_BWD_CASE(W, B)                                                                   \
+    if (wpr == W && bpl == B) {                                                               \
+        hipLaunchKernelGGL((bwd_kernel<W, B, MODE>), grid, dim3(threads), 0, st, a);          \
+        return launch_status();                                                               \
+    }
+    PACT_BWD_CASE(1, 1)
+    PACT_BWD_CASE(1, 2)
+    PACT_BWD_CASE(1, 3)
+    PACT_BWD_CASE(4, 1)
+    PACT_BWD_CASE(8, 1)
+    PACT_BWD_CASE(8, 2)
+    PACT_BWD_CASE(8, 3)
+    PACT_BWD_CASE(8, 4)
+#undef PACT_BWD_CASE
+    return PACT_ERR_UNSUPPORTED_SHAPE;
+}
+
+// Exposes dsilu32 for exhaustive verification.
+__global__ __launch_bounds__(256) void dsilu_probe_kernel(const uint16_t *g, float *out, int64_t n) {
+    __shared__ uint32_t tab[kSigTab];
+    load_dsilu_table(tab, threadIdx.x, 256);
+    lds_sync();
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = dsilu32_select(g[i], tab[silu32_index(g[i])]);
+}
+
+static CNV cnv_of(const pact_nvfp4 *q) {
+    CNV n;
+    n.codes = q->codes;
+    n.scales = q->scales;
+    n.d = q->row_scale;
+    return n;
+}
+
 static NV nv_of(const pact_nvfp4 *q) {
     NV n;
     n.codes = q ? q->codes : nullptr;
@@ -536,5 +864,70 @@ extern "C" pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64
     if (n == 0) return PACT_OK;
     const unsigned blocks = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(sigmoid_probe_kernel, dim3(blocks), dim3(256), 0, as_stream(stream), g, out, n);
+    return launch_status();
+}
+
+extern "C" pact_status pact_silu_mul_bwd_quant_nvfp4(const uint16_t *dh, int64_t ld_dh, const pact_nvfp4 *gq,
+                                                     const pact_nvfp4 *uq, int64_t rows, int64_t cols,
+                                                     uint16_t *dg, uint16_t *du, int64_t ld_out,
+                                                     const pact_nvfp4 *dgq, const pact_nvfp4 *duq, void *stream) {
+    PACT_TRY(check_row_len(rows, cols));
+    PACT_TRY(check_bf16(dh, ld_dh, cols));
+    PACT_TRY(check_nvfp4(gq, rows, cols));
+    PACT_TRY(check_nvfp4(uq, rows, cols));
+    if (dg) PACT_TRY(check_bf16(dg, ld_out, cols));
+    if (du) PACT_TRY(check_bf16(du, ld_out, cols));
+    PACT_TRY(check_nvfp4(dgq, rows, cols));
+    PACT_TRY(check_nvfp4(duq, rows, cols));
+    BwdArgs a = {};
+    a.dy = dh;
+    a.lddy = ld_dh;
+    a.in0 = cnv_of(gq);
+    a.in1 = cnv_of(uq);
+    a.o0 = dg;
+    a.o1 = du;
+    a.ldo = ld_out;
+    a.q0 = nv_of(dgq);
+    a.q1 = nv_of(duq);
+    a.rows = rows;
+    a.cols = (int)cols;
+    return launch_bwd<MODE_SILU_BWD>(a, as_stream(stream));
+}
+
+extern "C" pact_status pact_rmsnorm_bwd_nvfp4(const uint16_t *dy, int64_t ld_dy, const pact_nvfp4 *yq,
+                                              const uint16_t *gamma, const float *rstd, const uint16_t *C,
+                                              int64_t ld_c, int64_t rows, int64_t cols, uint16_t *dx,
+                                              int64_t ld_dx, const pact_nvfp4 *dxq, void *stream) {
+    PACT_TRY(check_row_len(rows, cols));
+    PACT_TRY(check_bf16(dy, ld_dy, cols));
+    PACT_TRY(check_nvfp4(yq, rows, cols));
+    PACT_TRY(check_bf16(gamma, cols, cols));
+    if (!rstd) return PACT_ERR_INVALID_ARG;
+    if (!aligned16(rstd)) return PACT_ERR_MISALIGNED;
+    if (C) PACT_TRY(check_bf16(C, ld_c, cols));
+    if (dx) PACT_TRY(check_bf16(dx, ld_dx, cols));
+    if (dxq) PACT_TRY(check_nvfp4(dxq, rows, cols));
+    if (!dx && !dxq) return PACT_ERR_INVALID_ARG;
+    BwdArgs a = {};
+    a.dy = dy;
+    a.lddy = ld_dy;
+    a.in0 = cnv_of(yq);
+    a.gamma = gamma;
+    a.rstd = rstd;
+    a.C = C;
+    a.ldc = ld_c;
+    a.o0 = dx;
+    a.ldo = ld_dx;
+    a.q0 = nv_of(dxq);
+    a.rows = rows;
+    a.cols = (int)cols;
+    return launch_bwd<MODE_RMS_BWD>(a, as_stream(stream));
+}
+
+extern "C" pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *stream) {
+    if (n < 0 || (n > 0 && (!g || !out))) return PACT_ERR_INVALID_ARG;
+    if (n == 0) return PACT_OK;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(dsilu_probe_kernel, dim3(blocks), dim3(256), 0, as_stream(stream), g, out, n);
     return launch_status();
 }

@@ -38,7 +38,8 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_rmsnorm_quant_nvfp4", "pact_silu_mul_quant_nvfp4",
            "pact_build_weight_layouts_workspace", "pact_build_weight_layouts",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
-           "pact_debug_sigmoid32", "pact_debug_gemm_plan"]
+           "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
+           "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32"]
 
 
 class PactError(RuntimeError):
@@ -79,6 +80,12 @@ def lib():
         L.pact_gemm_nvfp4_dgrad.argtypes = gemm_args
         L.pact_debug_sigmoid32.restype = st
         L.pact_debug_sigmoid32.argtypes = [P, P, I64, P]
+        L.pact_silu_mul_bwd_quant_nvfp4.restype = st
+        L.pact_silu_mul_bwd_quant_nvfp4.argtypes = [P, I64, NV, NV, I64, I64, P, P, I64, NV, NV, P]
+        L.pact_rmsnorm_bwd_nvfp4.restype = st
+        L.pact_rmsnorm_bwd_nvfp4.argtypes = [P, I64, NV, P, P, P, I64, I64, I64, P, I64, NV, P]
+        L.pact_debug_dsilu32.restype = st
+        L.pact_debug_dsilu32.argtypes = [P, P, I64, P]
         L.pact_debug_gemm_plan.restype = st
         L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
@@ -266,6 +273,51 @@ def pact_gemm_nvfp4_dgrad(dYq: NVFP4Tensor, W_bwd: NVFP4Tensor, dY=None, lora: L
     """dX = bf16(d_dy d_wb dYq.W_bwd^T + s bf16(dY B) A (+ C))."""
     return _gemm(lib().pact_gemm_nvfp4_dgrad, "pact_gemm_nvfp4_dgrad", dYq, dY, W_bwd, lora, C, dX,
                  ws, stream)
+
+
+def pact_silu_mul_bwd_quant_nvfp4(dh, gq: NVFP4Tensor, uq: NVFP4Tensor, dg=None, du=None, dgq=None,
+                                  duq=None, want_bf16=True, stream=None):
+    """dg = bf16((dh u') dsilu32(g')), du = bf16(dh sigma32(g')) from the NVFP4
+    gate/up stash (g', u' its BF16 values); dgq = Q(dg), duq = Q(du)."""
+    rows, cols = dh.shape
+    if want_bf16:
+        dg = dg if dg is not None else torch.empty((rows, cols), dtype=torch.bfloat16, device=dh.device)
+        du = du if du is not None else torch.empty((rows, cols), dtype=torch.bfloat16, device=dh.device)
+    dgq = dgq if dgq is not None else NVFP4Tensor.empty(rows, cols, dh.device)
+    duq = duq if duq is not None else NVFP4Tensor.empty(rows, cols, dh.device)
+    if dg is not None and du is not None:
+        assert _ld(dg) == _ld(du), "dg and du share one leading dimension"
+    ld_out = _ld(dg) if dg is not None else (_ld(du) if du is not None else cols)
+    a, b, c, d = gq.desc(), uq.desc(), dgq.desc(), duq.desc()
+    _check(lib().pact_silu_mul_bwd_quant_nvfp4(
+        _ptr(dh), _ld(dh), ctypes.byref(a), ctypes.byref(b), rows, cols, _ptr(dg), _ptr(du), ld_out,
+        ctypes.byref(c), ctypes.byref(d), _stream(stream)), "pact_silu_mul_bwd_quant_nvfp4")
+    return dg, du, dgq, duq
+
+
+def pact_rmsnorm_bwd_nvfp4(dy, yq: NVFP4Tensor, gamma, rstd, C=None, dx=None, dxq=None, want_dx=True,
+                           want_q=True, stream=None):
+    """dx = bf16((dy gamma - x^ c) rstd (+ C)), x^ = deq(yq)/gamma, c = mean(dy deq(yq));
+    dxq = Q(dx)."""
+    rows, cols = dy.shape
+    if want_dx and dx is None:
+        dx = torch.empty((rows, cols), dtype=torch.bfloat16, device=dy.device)
+    if want_q and dxq is None:
+        dxq = NVFP4Tensor.empty(rows, cols, dy.device)
+    a = yq.desc()
+    q = dxq.desc() if dxq is not None else None
+    _check(lib().pact_rmsnorm_bwd_nvfp4(
+        _ptr(dy), _ld(dy), ctypes.byref(a), _ptr(gamma), _ptr(rstd), _ptr(C), _ld(C) if C is not None else cols,
+        rows, cols, _ptr(dx), _ld(dx) if dx is not None else cols, ctypes.byref(q) if q is not None else None,
+        _stream(stream)), "pact_rmsnorm_bwd_nvfp4")
+    return dx, dxq
+
+
+def pact_debug_dsilu32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(g_bits.shape, dtype=torch.float32, device=g_bits.device)
+    _check(lib().pact_debug_dsilu32(_ptr(g_bits), _ptr(out), g_bits.numel(), _stream(stream)),
+           "pact_debug_dsilu32")
+    return out
 
 
 def pact_debug_sigmoid32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:

@@ -137,3 +137,30 @@ def test_gemm_plan_host_logic(L):
     assert L.pact_gemm_workspace(1024, 2048, 512, 16) >= parts + 2 * 16 * 1024  # the input-gradient direction
     assert L.pact_debug_gemm_plan(100, 200, 520, ctypes.byref(k), ctypes.byref(ks)) == 0
     assert ks.value == 1  # K % 64 != 0: no split
+
+
+def test_backward_validation(L):
+    """Argument checks of the backward entry points (host only, nothing is
+    launched on an error)."""
+    rows, cols = 4, 32
+    q = _nv(rows=rows, cols=cols)
+    bad = _nv(rows=rows, cols=cols + 16)
+    silu = L.pact_silu_mul_bwd_quant_nvfp4
+    ok = (FAKE, cols, ctypes.byref(q), ctypes.byref(q), rows, cols, FAKE, FAKE, cols,
+          ctypes.byref(q), ctypes.byref(q), None)
+    assert silu(FAKE, cols, ctypes.byref(q), ctypes.byref(q), rows, 24, FAKE, FAKE, cols,
+                ctypes.byref(q), ctypes.byref(q), None) == 2                   # cols % 16
+    assert silu(FAKE, cols, ctypes.byref(bad), ctypes.byref(q), *ok[4:]) == 1  # gq shape
+    assert silu(*ok[:9], None, ctypes.byref(q), None) == 1                    # dgq required
+    assert silu(FAKE + 8, *ok[1:]) == 3                                       # misaligned dh
+    rms = L.pact_rmsnorm_bwd_nvfp4
+    args = [FAKE, cols, ctypes.byref(q), FAKE, FAKE, None, cols, rows, cols, FAKE, cols, ctypes.byref(q), None]
+    a = list(args); a[9] = None; a[11] = None
+    assert rms(*a) == 1                                                       # no output
+    a = list(args); a[4] = None
+    assert rms(*a) == 1                                                       # rstd required
+    a = list(args); a[4] = FAKE + 4
+    assert rms(*a) == 3                                                       # misaligned rstd
+    a = list(args); a[2] = ctypes.byref(bad)
+    assert rms(*a) == 1                                                       # yq shape
+    assert L.pact_debug_dsilu32(None, FAKE, 4, None) == 1
