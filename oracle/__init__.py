@@ -86,6 +86,7 @@ def lib():
         L.orc_dot_bf16_f32.restype = ctypes.c_double
         L.orc_dot_bf16_f32.argtypes = [P, P, I64]
         L.orc_rmsnorm_bwd.argtypes = [P, I64, P, P, P, P, P, P, I64, I64, I64, P, P, P, P]
+        L.orc_lora_grads.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P, ctypes.c_int32, ctypes.c_float, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -334,3 +335,20 @@ def rmsnorm_bwd(dy: np.ndarray, yq: NVFP4, gamma: np.ndarray, rstd: np.ndarray, 
                           _p(_c(yq.d, np.float32)), _p(_c(gamma, np.uint16)), _p(_c(rstd, np.float32)),
                           _p(Cc), cols, rows, cols, _p(dx), _p(dxq.codes), _p(dxq.scales), _p(dxq.d))
     return dx, dxq
+
+
+# ---- LoRA weight gradients on the NVFP4 stash --------------------------------
+def lora_grads(xq: NVFP4, dY: np.ndarray, A: np.ndarray, B: np.ndarray, s: float):
+    """Returns (dA [r,K], dB [N,r]) in float64: dB = dY^T T^, dA = T'^T X^ with
+    X^ = bf16(deq(xq)), T^ = s bf16(X^ A^T), T' = s bf16(dY B)."""
+    dY = _c(dY, np.uint16)
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    M, N = dY.shape
+    r, K = A.shape
+    assert (xq.rows, xq.cols) == (M, K) and B.shape == (N, r)
+    dA = np.zeros((r, K), np.float64)
+    dB = np.zeros((N, r), np.float64)
+    lib().orc_lora_grads(_p(_c(xq.codes, np.uint8)), _p(_c(xq.scales, np.uint8)), _p(_c(xq.d, np.float32)),
+                         M, K, _p(dY), N, N, _p(A), _p(B), r, float(s), _p(dA), _p(dB))
+    return dA, dB

@@ -689,3 +689,52 @@ void orc_rmsnorm_bwd(const uint16_t *dy, int64_t ld, const uint8_t *yc, const ui
         free(xrow);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* LoRA weight gradients on the NVFP4 stash ([blog] Method bullet 2 and final */
+/* note: the activations kept for backward are the NVFP4 copies, the adapters */
+/* are BF16; [peft] LoRA: h = W0 x + B A x, so dB = dY^T (A x)^T-side and      */
+/* dA = (B^T dY)-side x^T).                                                   */
+/* Readings: the LoRA input is the stash dequantized and taken in BF16,       */
+/* X^ = bf16(deq(Xq)) (the BF16 X is not kept); the rank-r intermediates are   */
+/* rounded to BF16 like the forward's (T^ = s bf16(X^ A^T), T' = s bf16(dY B)); */
+/* dB = dY^T T^ [N, r] and dA = T'^T X^ [r, K]; the reference sums in binary64.*/
+/* ------------------------------------------------------------------------- */
+void orc_lora_grads(const uint8_t *xc, const uint8_t *xs, const float *xd, int64_t M, int64_t K,
+                    const uint16_t *dY, int64_t ld_dy, int64_t N, const uint16_t *A, const uint16_t *B,
+                    int32_t r, float s, double *dA, double *dB) {
+    assert(K % 16 == 0 && r > 0);
+    float *Xh = (float *)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+    float *Th = (float *)malloc(sizeof(float) * (size_t)(M * r));
+    float *Tp = (float *)malloc(sizeof(float) * (size_t)(M * r));
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            Xh[m * K + k] = orc_bf16_to_f32(orc_f32_to_bf16(deq_elem(xc + m * (K / 2), xs + m * (K / 16), xd[m], k)));
+        for (int32_t j = 0; j < r; ++j) {
+            float t = 0.0f, u = 0.0f;
+            for (int64_t k = 0; k < K; ++k) t = t + Xh[m * K + k] * orc_bf16_to_f32(A[j * K + k]);
+            for (int64_t n = 0; n < N; ++n)
+                u = u + orc_bf16_to_f32(dY[m * ld_dy + n]) * orc_bf16_to_f32(B[n * r + j]);
+            Th[m * r + j] = s * orc_bf16_to_f32(orc_f32_to_bf16(t));
+            Tp[m * r + j] = s * orc_bf16_to_f32(orc_f32_to_bf16(u));
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int32_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m) acc += (double)orc_bf16_to_f32(dY[m * ld_dy + n]) * (double)Th[m * r + j];
+            dB[n * r + j] = acc;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int32_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m) acc += (double)Tp[m * r + j] * (double)Xh[m * K + k];
+            dA[j * K + k] = acc;
+        }
+    free(Xh);
+    free(Th);
+    free(Tp);
+}

@@ -117,6 +117,14 @@ void  orc_rmsnorm_bwd(const uint16_t *dy, int64_t ld, const uint8_t *yc, const u
                       const uint16_t *C, int64_t ldc, int64_t rows, int64_t cols, uint16_t *dx,
                       uint8_t *dxc, uint8_t *dxs, float *dxd);
 
+/* ---- LoRA weight gradients on the NVFP4 stash ([blog] Method, bullet 2 and
+ * final note; [peft] LoRA) ----
+ * X^ = bf16(deq(Xq)) [M,K]; T^ = s bf16(X^ A^T), T' = s bf16(dY B) [M,r];
+ * dB = dY^T T^ [N,r], dA = T'^T X^ [r,K], summed in binary64. */
+void orc_lora_grads(const uint8_t *xc, const uint8_t *xs, const float *xd, int64_t M, int64_t K,
+                    const uint16_t *dY, int64_t ld_dy, int64_t N, const uint16_t *A, const uint16_t *B,
+                    int32_t r, float s, double *dA, double *dB);
+
 int orc_num_threads(void);
 
 #ifdef __cplusplus

@@ -156,3 +156,41 @@ def test_rmsnorm_bwd_residual_and_zero():
     zero = synth.to_bf16_bits(np.zeros((rows, cols)))
     dxz, dxq = oracle.rmsnorm_bwd(zero, yq, gamma, rstd)
     assert np.all(_f32(dxz) == 0.0) and np.all(dxq.d == 0.0)
+
+
+def _lora_case(rng, M, N, K, r):
+    x = synth.to_bf16_bits(rng.standard_t(4, (M, K)) * 0.5)
+    xq = oracle.quantize_bf16(x)
+    dY = synth.to_bf16_bits(rng.standard_normal((M, N)))
+    A = synth.to_bf16_bits(0.02 * rng.standard_normal((r, K)))
+    B = synth.to_bf16_bits(0.01 * rng.standard_normal((N, r)))
+    return xq, dY, A, B
+
+
+def test_lora_grads_against_autograd():
+    """dA, dB of sum(dY * s (X^ A^T) B^T) by float64 autograd, X^ the BF16
+    values of the dequantized stash; the oracle's BF16 intermediates stay
+    within a BF16 rounding of it (relative to the gradient's scale)."""
+    rng = np.random.default_rng(21)
+    M, N, K, r, s = 40, 48, 64, 8, 2.0
+    xq, dY, A, B = _lora_case(rng, M, N, K, r)
+    dA, dB = oracle.lora_grads(xq, dY, A, B, s)
+    X = torch.tensor(_f32(synth.to_bf16_bits(oracle.dequantize(xq).astype(np.float64))).astype(np.float64))
+    tA = torch.tensor(_f32(A).astype(np.float64), requires_grad=True)
+    tB = torch.tensor(_f32(B).astype(np.float64), requires_grad=True)
+    loss = (torch.tensor(_f32(dY).astype(np.float64)) * (s * (X @ tA.T) @ tB.T)).sum()
+    loss.backward()
+    for got, ref in ((dA, tA.grad.numpy()), (dB, tB.grad.numpy())):
+        assert np.max(np.abs(got - ref)) <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
+def test_lora_grads_zero_adapters():
+    """B = 0 gives dA = 0 exactly (T' = 0); A = 0 gives dB = 0 exactly."""
+    rng = np.random.default_rng(22)
+    xq, dY, A, B = _lora_case(rng, 16, 32, 32, 4)
+    zA = np.zeros_like(A)
+    zB = np.zeros_like(B)
+    dA, dB = oracle.lora_grads(xq, dY, A, zB, 2.0)
+    assert np.all(dA == 0.0) and np.any(dB != 0.0)
+    dA, dB = oracle.lora_grads(xq, dY, zA, B, 2.0)
+    assert np.all(dB == 0.0) and np.any(dA != 0.0)
