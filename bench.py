@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: the whole batch, at most 1024)")
+    ap.add_argument("--lora-grads", action="store_true",
+                    help="add the LoRA weight gradients (dA, dB of every projection, from the NVFP4 stash) "
+                         "to each layer's backward; timed as their own kind, never counted as frozen FLOPs")
     ap.add_argument("--eager", action="store_true",
                     help="time the step without graph capture")
     ap.add_argument("--no-isolated", action="store_true",
@@ -100,7 +103,7 @@ def nvb(rows, cols):
 class Stack:
     """Device buffers, weights and the step schedule of `layers` decoder layers."""
 
-    def __init__(self, shape, seed, layers):
+    def __init__(self, shape, seed, layers, lora_grads=False):
         import torch
         from nvfp4_gemm_amd import pact as pb
         from nvfp4_gemm_amd import synth
@@ -152,6 +155,15 @@ class Stack:
         self.dxs = [self.dout, E(M, H), E(M, H)]
         need = max(pb.pact_gemm_workspace(M, n, k, shape.rank) for n, k in shape.projections().values())
         self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        self.lora_grads = lora_grads
+        if lora_grads:  # one dA/dB pair per projection, overwritten by every layer
+            r = shape.rank
+            self.gA = {n: torch.empty((r, k), dtype=torch.float32, device=dev)
+                       for n, (_, k) in shape.projections().items()}
+            self.gB = {n: torch.empty((nn, r), dtype=torch.float32, device=dev)
+                       for n, (nn, _) in shape.projections().items()}
+            gneed = max(pb.pact_lora_grads_workspace(M, n, k, r) for n, k in shape.projections().values())
+            self.gws = torch.empty((max(gneed, 16),), dtype=torch.uint8, device=dev)
 
     def calls(self):
         """The step as a list of (kind, frozen flops, bytes, fn, lora flops)."""
@@ -161,6 +173,15 @@ class Stack:
         gemm_fl = lambda n, k: 2 * M * n * k
         lora_fl = lambda n, k: 2 * M * r * (n + k)
         c = []
+
+        def grads(nm, xq, dY, L):
+            """dA, dB of projection nm (input xq from the stash, output gradient dY)."""
+            if not self.lora_grads:
+                return
+            n, k = S.projections()[nm]
+            c.append(("lora_grads", 0, nvb(M, k) + 2 * M * n + 4 * r * (n + k) + 4 * r * (n + k),
+                      lambda nm=nm, xq=xq, dY=dY, L=L: pb.pact_lora_grads_nvfp4(
+                          xq, dY, L[nm], dA=self.gA[nm], dB=self.gB[nm], ws=self.gws), 4 * M * r * (n + k)))
         xin = lambda l: self.xs[0] if l == 0 else self.xs[1 + (l - 1) % 2]
         xout = lambda l: self.xs[1 + l % 2]
         for l in range(self.L):
@@ -200,18 +221,22 @@ class Stack:
                           lambda dout=dout: pb.pact_quantize_nvfp4(dout, self.doq), 0))
             c.append(("gemm_dgrad", gemm_fl(H, I), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.doq, Wb["down"], dY=dout, lora=L["down"], dX=self.dh, ws=ws), lora_fl(H, I)))
+            grads("down", st["hq"], dout, L)
             c.append(("silu_mul_bwd", 0, M * I * 2 + 2 * nvb(M, I) + 2 * M * I * 2 + 2 * nvb(M, I),
                       lambda st=st: pb.pact_silu_mul_bwd_quant_nvfp4(self.dh, st["gq"], st["uq"], self.dg, self.du,
                                                                      self.dgq, self.duq), 0))
             c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dgq, Wb["gate"], dY=self.dg, lora=L["gate"], dX=self.dn, ws=ws), lora_fl(I, H)))
+            grads("gate", st["n2q"], self.dg, L)
             c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.duq, Wb["up"], dY=self.du, lora=L["up"], C=self.dn, dX=self.dn, ws=ws), lora_fl(I, H)))
+            grads("up", st["n2q"], self.du, L)
             c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2 + nvb(M, H),
                       lambda st=st, l=l, dout=dout: pb.pact_rmsnorm_bwd_nvfp4(
                           self.dn, st["n2q"], self.g2[l], st["rstd2"], C=dout, dx=self.dx2, dxq=self.dx2q), 0))
             c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dx2q, Wb["o"], dY=self.dx2, lora=L["o"], dX=self.da, ws=ws), lora_fl(H, H)))
+            grads("o", st["aq"], self.dx2, L)
             dq, dk, dv = self.da, self.da[:, :KV], self.da[:, KV:2 * KV]
             c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda dq=dq: pb.pact_quantize_nvfp4(dq, self.dqq), 0))
             c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dk=dk: pb.pact_quantize_nvfp4(dk, self.dkq), 0))
@@ -222,6 +247,9 @@ class Stack:
                 self.dkq, Wb["k"], dY=dk, lora=L["k"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
             c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dvq, Wb["v"], dY=dv, lora=L["v"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
+            grads("q", st["n1q"], dq, L)
+            grads("k", st["n1q"], dk, L)
+            grads("v", st["n1q"], dv, L)
             last = j == self.L - 1
             c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2
                       + (0 if last else nvb(M, H)),
@@ -244,7 +272,9 @@ class Stack:
         return {"workload": S.name, "layers": self.L, "tokens": S.tokens, "hidden": S.hidden,
                 "intermediate": S.inter, "kv": S.kv, "lora_rank": S.rank, "lora_scale": S.lora_scale,
                 "step": "forward + input-gradient backward of every layer, 7 frozen NVFP4 projections "
-                        "per layer with BF16 LoRA, fused RMSNorm/SiLU quantizers"}
+                        "per layer with BF16 LoRA, fused RMSNorm/SiLU quantizers"
+                        + (", plus the LoRA weight gradients of every projection" if self.lora_grads else ""),
+                "lora_grads": self.lora_grads}
 
 
 class Linear:
@@ -509,7 +539,7 @@ def main():
         work = Linear(args.seed)
     else:
         shape = synth.LAYERS[args.config]
-        work = Stack(shape, args.seed, shape.layers)
+        work = Stack(shape, args.seed, shape.layers, lora_grads=args.lora_grads)
     st = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     calls = work.calls()
@@ -581,6 +611,8 @@ def main():
         d = {"avg_us": 1e3 * k["ms"] / k["calls"], "calls_per_step": k["calls"] // args.steps}
         if k["flops"]:
             d["frozen_tflops"] = k["flops"] / (k["ms"] * 1e-3) / 1e12
+        elif k["lora_flops"]:
+            d["lora_tflops"] = k["lora_flops"] / (k["ms"] * 1e-3) / 1e12
         if k["bytes"]:
             gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
             d["GB/s"] = gbs

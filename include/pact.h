@@ -212,6 +212,25 @@ pact_status pact_rmsnorm_bwd_nvfp4(const uint16_t *dy, int64_t ld_dy, const pact
                                    int64_t ld_c, int64_t rows, int64_t cols, uint16_t *dx,
                                    int64_t ld_dx, const pact_nvfp4 *dxq, void *stream);
 
+/* Workspace bytes of pact_lora_grads_nvfp4 for M tokens, output width N,
+ * input width K and LoRA rank r (0 when r <= 0). */
+size_t pact_lora_grads_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* LoRA weight gradients of one projection on the NVFP4 stash (blog "Method",
+ * second bullet and closing paragraph: activations kept for backward are the
+ * NVFP4 copies, adapters stay BF16; PEFT explainer: the update B A x):
+ *   X^ = bf16(deq(Xq)) [M][K],  T^ = bf16(s X^ A^T),  T' = bf16(s dY B)  [M][r],
+ *   dB = dY^T T^  [N][r],   dA = T'^T X^  [r][K],
+ * FP32 sums over the tokens (fixed order for a given shape), FP32 outputs.
+ * Xq: the projection's input as stashed by the forward (NVFP4 [M][K]); dY
+ * [M][N] BF16 (ld_dy): the gradient of the projection's output; lora: A [r][K],
+ * B [N][r], scale s; dA [r][K] and dB [N][r] FP32, row-major.  K % 16 == 0,
+ * N % 16 == 0, 1 <= r <= 64.  Empty M gives zero gradients.  The workspace
+ * (pact_lora_grads_workspace bytes) holds X^, T^, T' and partial sums. */
+pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int64_t ld_dy, int64_t N,
+                                  const pact_lora *lora, float *dA, float *dB, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 /* Diagnostic: out[i] = sigma32(g[i]) (the binary32 sigmoid-times-input the
  * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
  * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */

@@ -36,16 +36,6 @@
 
 namespace pact {
 
-struct DownArgs {
-    const uint16_t *X;  // nullptr: no fused LoRA-down
-    int64_t ldx;
-    int M, Kl;
-    const uint16_t *Ps;
-    int64_t p_sj, p_sk;
-    int r, rpad, j0;
-    float scale;
-    uint16_t *T;
-};
 
 struct GemmArgs {
     const uint8_t *a_codes;
@@ -423,7 +413,7 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
     lora_down_rows<RG, kDownWaves>(d, blockIdx.x * 16, red);
 }
 
-static pact_status launch_lora_down(DownArgs d, hipStream_t st) {
+pact_status launch_lora_down(DownArgs d, hipStream_t st) {
     const dim3 grid((unsigned)((d.M + 15) / 16)), block(64 * kDownWaves);
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         d.j0 = j0;

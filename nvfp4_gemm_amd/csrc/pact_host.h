@@ -44,6 +44,21 @@ inline pact_status launch_status() {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// LoRA-down product T [M][rpad] = bf16(s . (X [M][Kl] . P^T)) over ranks
+// j0 .. j0 + 64 (P(j, k) = Ps[j p_sj + k p_sk], zero for j >= r); launched by
+// launch_lora_down (all ranks) and fused into split-K GEMM launches.
+struct DownArgs {
+    const uint16_t *X;  // nullptr: no fused LoRA-down
+    int64_t ldx;
+    int M, Kl;
+    const uint16_t *Ps;
+    int64_t p_sj, p_sk;
+    int r, rpad, j0;
+    float scale;
+    uint16_t *T;
+};
+pact_status launch_lora_down(DownArgs d, hipStream_t st);
+
 // Compute units of the current device (a host-side property query; 256 when
 // the query fails).
 inline int device_cus() {

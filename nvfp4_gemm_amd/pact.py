@@ -39,7 +39,8 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_build_weight_layouts_workspace", "pact_build_weight_layouts",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
-           "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32"]
+           "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
+           "pact_lora_grads_nvfp4"]
 
 
 class PactError(RuntimeError):
@@ -84,6 +85,10 @@ def lib():
         L.pact_silu_mul_bwd_quant_nvfp4.argtypes = [P, I64, NV, NV, I64, I64, P, P, I64, NV, NV, P]
         L.pact_rmsnorm_bwd_nvfp4.restype = st
         L.pact_rmsnorm_bwd_nvfp4.argtypes = [P, I64, NV, P, P, P, I64, I64, I64, P, I64, NV, P]
+        L.pact_lora_grads_workspace.restype = ctypes.c_size_t
+        L.pact_lora_grads_workspace.argtypes = [I64, I64, I64, ctypes.c_int32]
+        L.pact_lora_grads_nvfp4.restype = st
+        L.pact_lora_grads_nvfp4.argtypes = [NV, P, I64, I64, LO, P, P, P, ctypes.c_size_t, P]
         L.pact_debug_dsilu32.restype = st
         L.pact_debug_dsilu32.argtypes = [P, P, I64, P]
         L.pact_debug_gemm_plan.restype = st
@@ -311,6 +316,27 @@ def pact_rmsnorm_bwd_nvfp4(dy, yq: NVFP4Tensor, gamma, rstd, C=None, dx=None, dx
         rows, cols, _ptr(dx), _ld(dx) if dx is not None else cols, ctypes.byref(q) if q is not None else None,
         _stream(stream)), "pact_rmsnorm_bwd_nvfp4")
     return dx, dxq
+
+
+def pact_lora_grads_workspace(M: int, N: int, K: int, r: int) -> int:
+    return int(lib().pact_lora_grads_workspace(M, N, K, r))
+
+
+def pact_lora_grads_nvfp4(Xq: NVFP4Tensor, dY, lora: LoRA, dA=None, dB=None, ws=None, stream=None):
+    """dB = dY^T bf16(s X^ A^T) [N, r] and dA = bf16(s dY B)^T X^ [r, K], FP32,
+    with X^ the BF16 values of the stashed NVFP4 input."""
+    M, N = dY.shape
+    K, r = Xq.cols, lora.r
+    if dA is None:
+        dA = torch.empty((r, K), dtype=torch.float32, device=dY.device)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.float32, device=dY.device)
+    if ws is None:
+        ws = torch.empty((max(pact_lora_grads_workspace(M, N, K, r), 16),), dtype=torch.uint8, device=dY.device)
+    dx, dl = Xq.desc(), lora.desc()
+    _check(lib().pact_lora_grads_nvfp4(ctypes.byref(dx), _ptr(dY), _ld(dY), N, ctypes.byref(dl), _ptr(dA),
+                                       _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)), "pact_lora_grads_nvfp4")
+    return dA, dB
 
 
 def pact_debug_dsilu32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:

@@ -164,3 +164,21 @@ def test_backward_validation(L):
     a = list(args); a[2] = ctypes.byref(bad)
     assert rms(*a) == 1                                                       # yq shape
     assert L.pact_debug_dsilu32(None, FAKE, 4, None) == 1
+
+
+def test_lora_grads_validation(L):
+    """Argument checks of the LoRA-gradient entry point (host only)."""
+    M, N, K, r = 8, 32, 64, 4
+    q = _nv(rows=M, cols=K)
+    lo = pb.pact_lora(FAKE, FAKE, r, 2.0)
+    f = L.pact_lora_grads_nvfp4
+    need = L.pact_lora_grads_workspace(M, N, K, r)
+    assert need >= M * K * 2                                                  # holds X^ in BF16
+    assert L.pact_lora_grads_workspace(M, N, K, 0) == 0
+    assert f(ctypes.byref(q), FAKE, N, N, None, FAKE, FAKE, FAKE, need, None) == 1        # no adapter
+    big = pb.pact_lora(FAKE, FAKE, 65, 2.0)
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(big), FAKE, FAKE, FAKE, need, None) == 2  # r > 64
+    assert f(ctypes.byref(q), FAKE, N, 24, ctypes.byref(lo), FAKE, FAKE, FAKE, need, None) == 2  # N % 16
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE + 4, FAKE, FAKE, need, None) == 3  # dA
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need - 1, None) == 4  # workspace
+    assert f(ctypes.byref(q), FAKE, N - 8, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need, None) == 1  # ld < N
