@@ -226,7 +226,8 @@ size_t pact_lora_grads_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
  * [M][N] BF16 (ld_dy): the gradient of the projection's output; lora: A [r][K],
  * B [N][r], scale s; dA [r][K] and dB [N][r] FP32, row-major.  K % 16 == 0,
  * N % 16 == 0, 1 <= r <= 64.  Empty M gives zero gradients.  The workspace
- * (pact_lora_grads_workspace bytes) holds X^, T^, T' and partial sums. */
+ * (pact_lora_grads_workspace bytes) holds T^, T', B^T and partial sums; X^ is
+ * decoded in registers, never stored. */
 pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int64_t ld_dy, int64_t N,
                                   const pact_lora *lora, float *dA, float *dB, void *ws,
                                   size_t ws_bytes, void *stream);

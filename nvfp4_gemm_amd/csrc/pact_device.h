@@ -109,6 +109,27 @@ __device__ __forceinline__ void dequant16(uint32_t c0, uint32_t c1, uint32_t sca
     }
 }
 
+// 8 dequantized values of one 8-code dword, rounded to BF16 (four words, low
+// half first): bf16(fl32((code x scale in FP16) x d)), as dequant16.
+__device__ __forceinline__ u32x4 dequant8_bf16(uint32_t w, half2_t sc, float d) {
+    const half8_t h = decode8(w, sc);
+    u32x4 r;
+    r.x = f32x2_to_bf16x2((float)h[0] * d, (float)h[1] * d);
+    r.y = f32x2_to_bf16x2((float)h[2] * d, (float)h[3] * d);
+    r.z = f32x2_to_bf16x2((float)h[4] * d, (float)h[5] * d);
+    r.w = f32x2_to_bf16x2((float)h[6] * d, (float)h[7] * d);
+    return r;
+}
+
+// FP16 pair (both halves) of an E4M3 scale byte.
+__device__ __forceinline__ half2_t e4m3_to_h2(uint32_t byte) {
+    const half2_t sh = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)byte, 1.0f, false);
+    half2_t sc;
+    sc[0] = sh[0];
+    sc[1] = sh[0];
+    return sc;
+}
+
 // Per-row parameters of the quantizer.
 struct RowQ {
     float d;    // row scale

@@ -413,7 +413,197 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
     lora_down_rows<RG, kDownWaves>(d, blockIdx.x * 16, red);
 }
 
+// Standalone LoRA-down for up to 64 ranks with contiguous rows of P
+// (p_sk == 1).  Its cost is the number of vector memory instructions in
+// flight per CU, and the rank operand P costs as many instructions as X (it is
+// read from L2 by every row group).  So: a wavefront takes RPW row groups and
+// uses every P fragment for all of them; NW = 4 wavefronts split K; each
+// wavefront works through its K range in stages of 128 K with the loads of
+// the next stage issued before the MFMAs of the current one (branch-free: out
+// of range fragments read a clamped address and are zeroed).  Within a stage,
+// fragment c of lane group g covers 8 K at kpos(c, g): for BF16 rows a
+// row's 64 contiguous bytes per instruction; for NVFP4 rows the lane's 16
+// code bytes hold its 32 K (decoded to BF16 in registers).
+constexpr int kPipeWaves = 4;
+
+template <bool NV>
+__device__ __forceinline__ int down_kpos(int c, int g) { return NV ? 32 * g + 8 * c : 32 * c + 8 * g; }
+
+template <int RG, int RPW, bool NV>
+__global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArgs d) {
+    constexpr int NW = kPipeWaves;
+    constexpr int RS = 16 * RG + 1;
+    constexpr int ROWS = 16 * RPW;
+    __shared__ float red[NW * ROWS * RS];
+    const int groups = (d.M + ROWS - 1) / ROWS;
+    if (NV && (int)blockIdx.x >= groups) {  // side work (whole workgroups, before any barrier)
+        const int64_t i = (int64_t)(blockIdx.x - groups) * blockDim.x + threadIdx.x;
+        const int64_t nt = (int64_t)d.side_N * d.side_r;
+        if (i < nt) {
+            const int j = (int)(i / d.side_N), n = (int)(i % d.side_N);
+            d.side_Bt[i] = d.side_B[(int64_t)n * d.side_r + j];
+        }
+        return;
+    }
+    const int m0 = blockIdx.x * ROWS;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int li = lane & 15, g = lane >> 4;
+    const int ks = ((d.Kl + NW - 1) / NW + 127) / 128 * 128;
+    const int kb = w * ks, ke = min(d.Kl, kb + ks);
+    int row[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) row[q] = min(m0 + 16 * q + li, d.M - 1);
+    const uint16_t *pr[RG];
+    bool jok[RG];
+#pragma unroll
+    for (int f = 0; f < RG; ++f) {
+        const int j = d.j0 + 16 * f + li;
+        jok[f] = j < d.r;
+        pr[f] = d.Ps + (int64_t)min(j, d.r - 1) * d.p_sj;
+    }
+    float xdm[RPW];
+    if (NV) {
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) xdm[q] = d.xd[row[q]];
+    }
+    const bool k32 = (d.Kl & 31) == 0;  // NVFP4 rows start 16-byte (codes) and 2-byte (scales) aligned
+    float4_t acc[RPW][RG];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int f = 0; f < RG; ++f) acc[q][f] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // stage buffers: X fragments (BF16) or raw NVFP4 (16 code bytes + 2 scale bytes), P fragments
+    u32x4 xv[2][RPW][NV ? 1 : 4];
+    uint32_t xs[2][RPW];
+    u32x4 pv[2][4][RG];
+    auto load = [&](int b, int kc) {
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            if (NV) {
+                const int k0 = kc + 32 * g;
+                const int kk = k0 < ke ? k0 : 0;
+                const uint8_t *cr = d.xc + (int64_t)row[q] * (d.Kl / 2) + kk / 2;
+                const uint8_t *sr = d.xs + (int64_t)row[q] * (d.Kl / 16) + kk / 16;
+                uint32_t s2;
+                if (k32) {
+                    xv[b][q][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cr));
+                    s2 = *reinterpret_cast<const uint16_t *>(sr);
+                } else {  // rows of 16 K multiples: the second block may be past the row
+                    const bool two = kk + 16 < d.Kl;
+                    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(cr));
+                    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr));
+                    xv[b][q][0] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    s2 = (uint32_t)sr[0] | ((uint32_t)sr[two ? 1 : 0] << 8);
+                }
+                // blocks at or past the end of the K range decode to zero (scale 0)
+                if (k0 >= ke) s2 = 0u;
+                else if (k0 + 16 >= ke) s2 &= 0xFFu;
+                xs[b][q] = s2;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int k = kc + down_kpos<NV>(c, g);
+                    const u32x4 v = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(d.X + (int64_t)row[q] * d.ldx + (k < ke ? k : 0)));
+                    xv[b][q][c] = k < ke ? v : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int k = kc + down_kpos<NV>(c, g);
+#pragma unroll
+            for (int f = 0; f < RG; ++f) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(pr[f] + (k < ke ? k : 0));
+                pv[b][c][f] = (k < ke && jok[f]) ? v : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto mma = [&](int b) {
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            half2_t sc0, sc1;
+            if (NV) {
+                sc0 = e4m3_to_h2(xs[b][q] & 0xFFu);
+                sc1 = e4m3_to_h2(xs[b][q] >> 8);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                u32x4 xf;
+                if (NV) xf = dequant8_bf16(xv[b][q][0][c], c < 2 ? sc0 : sc1, xdm[q]);
+                else xf = xv[b][q][c];
+#pragma unroll
+                for (int f = 0; f < RG; ++f)
+                    acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xf),
+                                                                        __builtin_bit_cast(bf16x8_t, pv[b][c][f]),
+                                                                        acc[q][f], 0, 0, 0);
+            }
+        }
+    };
+    if (kb < ke) {
+        load(0, kb);
+        for (int kc = kb;;) {
+            if (kc + 128 >= ke) {
+                mma(0);
+                break;
+            }
+            load(1, kc + 128);
+            mma(0);
+            kc += 128;
+            if (kc + 128 >= ke) {
+                mma(1);
+                break;
+            }
+            load(0, kc + 128);
+            mma(1);
+            kc += 128;
+        }
+    }
+    // accumulator element e of lane (li, g): row 4 g + e of the group, rank 16 f + li
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int f = 0; f < RG; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[(w * ROWS + 16 * q + 4 * g + e) * RS + 16 * f + li] = acc[q][f][e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < ROWS * 16 * RG; i += 64 * NW) {
+        const int mi = i / (16 * RG), ji = i % (16 * RG);
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) sum += red[(q * ROWS + mi) * RS + ji];
+        const float ts = d.scale * sum;
+        if (m0 + mi < d.M) d.T[(int64_t)(m0 + mi) * d.rpad + d.j0 + ji] = (uint16_t)f32_to_bf16_bits(ts);
+    }
+}
+
+template <bool NV>
+static pact_status launch_down_pipe(DownArgs d, hipStream_t st) {
+    const int rg = d.rpad / 16;
+    const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
+    const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) + (NV ? d.side_wgs : 0))),
+        block(64 * kPipeWaves);
+    d.j0 = 0;
+#define PACT_DOWN_PIPE(RG)                                                                        \
+    if (two) hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 2, NV>), grid, block, 0, st, d);      \
+    else hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 1, NV>), grid, block, 0, st, d);
+    switch (rg) {
+        case 1: PACT_DOWN_PIPE(1) break;
+        case 2: PACT_DOWN_PIPE(2) break;
+        case 3: PACT_DOWN_PIPE(3) break;
+        default: PACT_DOWN_PIPE(4) break;
+    }
+#undef PACT_DOWN_PIPE
+    return launch_status();
+}
+
+pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st) {
+    if (d.rpad > 64 || d.p_sk != 1 || !d.xc) return PACT_ERR_UNSUPPORTED_SHAPE;
+    return launch_down_pipe<true>(d, st);
+}
+
 pact_status launch_lora_down(DownArgs d, hipStream_t st) {
+    if (d.rpad <= 64 && d.p_sk == 1) return launch_down_pipe<false>(d, st);
     const dim3 grid((unsigned)((d.M + 15) / 16)), block(64 * kDownWaves);
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         d.j0 = j0;

@@ -46,7 +46,9 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // LoRA-down product T [M][rpad] = bf16(s . (X [M][Kl] . P^T)) over ranks
 // j0 .. j0 + 64 (P(j, k) = Ps[j p_sj + k p_sk], zero for j >= r); launched by
-// launch_lora_down (all ranks) and fused into split-K GEMM launches.
+// launch_lora_down (all ranks) and fused into split-K GEMM launches.  X is
+// BF16 rows, or (launch_lora_down_nvfp4) the BF16 values of NVFP4 rows:
+// X(m, k) = bf16(fl32((code x block scale) x d_m)).
 struct DownArgs {
     const uint16_t *X;  // nullptr: no fused LoRA-down
     int64_t ldx;
@@ -56,8 +58,17 @@ struct DownArgs {
     int r, rpad, j0;
     float scale;
     uint16_t *T;
+    const uint8_t *xc, *xs;  // NVFP4 source: codes [M][Kl/2], scales [M][Kl/16]
+    const float *xd;         // and row scales [M]
+    // extra workgroups of launch_lora_down_nvfp4 (side_wgs of them) write
+    // Bt [side_r][side_N] = B^T (B [side_N][side_r])
+    int side_wgs;
+    const uint16_t *side_B;
+    uint16_t *side_Bt;
+    int side_N, side_r;
 };
 pact_status launch_lora_down(DownArgs d, hipStream_t st);
+pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st);
 
 // Compute units of the current device (a host-side property query; 256 when
 // the query fails).

@@ -5,132 +5,219 @@
 // paragraph: the activations kept for backward are NVFP4 copies and the
 // adapters stay BF16; kongchang.com PEFT explainer: the LoRA update B A x.)
 //
-// Both gradients are contractions over the tokens m of row-major [M][C]
-// matrices with the rank-r intermediate [M][rpad]: out[c][j] = sum_m V[m][c]
-// T[m][j].  They run on v_mfma_f32_32x32x16_bf16 with D = out (32 columns c x
-// 32 ranks j per tile): lane (h, l) of the A operand holds V[m0 + 8h + e][c0 + l]
-// for e < 8 and of the B operand T[m0 + 8h + e][32 t + l] (the same token
-// assignment in both, so the dot products are unchanged); those are 2-byte
-// loads, coalesced across the 32 lanes of a row.  The tokens of a column
-// block are split across the 4 wavefronts of a workgroup (summed through LDS
-// in wavefront order) and across msplit workgroups (FP32 partials summed in
-// split order by a second kernel), so every run adds in the same order.
+// X^ is never materialized: the LoRA-down of T^ and the contraction for dA
+// decode the NVFP4 rows in registers.  Five launches: T^ (LoRA-down of the
+// NVFP4 rows, whose extra workgroups also write B^T), T' (LoRA-down of dY),
+// the token contraction for dB, the one for dA (whose extra workgroups sum
+// dB's token splits in order), and the in-order sum of dA's splits.
 #include "pact_device.h"
 #include "pact_host.h"
 
 namespace pact {
 
-// X^ = bf16(deq(Xq)): one thread per 16-element block.
-__global__ __launch_bounds__(256) void dequant_bf16_kernel(const uint8_t *codes, const uint8_t *scales,
-                                                           const float *d, int64_t rows, int cols, uint16_t *out) {
-    const int nb = cols >> 4;
-    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (blk >= rows * nb) return;
-    const int64_t row = blk / nb;
-    const int b = (int)(blk - row * nb);
-    const u32x2 c = *reinterpret_cast<const u32x2 *>(codes + row * (cols / 2) + 8 * b);
-    float R[16];
-    dequant16(c.x, c.y, scales[row * (cols / 16) + b], d[row], R);
-    u32x4 lo, hi;
-    lo.x = f32x2_to_bf16x2(R[0], R[1]);
-    lo.y = f32x2_to_bf16x2(R[2], R[3]);
-    lo.z = f32x2_to_bf16x2(R[4], R[5]);
-    lo.w = f32x2_to_bf16x2(R[6], R[7]);
-    hi.x = f32x2_to_bf16x2(R[8], R[9]);
-    hi.y = f32x2_to_bf16x2(R[10], R[11]);
-    hi.z = f32x2_to_bf16x2(R[12], R[13]);
-    hi.w = f32x2_to_bf16x2(R[14], R[15]);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(out + row * cols + 16 * b);
-    dst[0] = lo;
-    dst[1] = hi;
+constexpr int kMaxSplits = 32;
+
+// out[c * osc + j * osj] = sum over splits s = 0, 1, ... of part[s][c][j]
+// (j < r, part rows of jw floats): the reduction of a token-split contraction.
+struct RedArgs {
+    const float *part;
+    int ms, C, r, jw;
+    float *out;
+    int64_t osc, osj;
+    int wgs;  // workgroups doing it
+};
+
+// One output per thread; all of its partials are loaded before the in-order sum.
+__device__ __forceinline__ void reduce_splits(const RedArgs &a, int64_t i) {
+    if (i >= (int64_t)a.C * a.r) return;
+    const int cc = (int)(i / a.r), j = (int)(i % a.r);
+    const float *src = a.part + (int64_t)cc * a.jw + j;
+    const int64_t step = (int64_t)a.C * a.jw;
+    float v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) v[s] = s < a.ms ? src[s * step] : 0.0f;
+    float sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < a.ms) sum += v[s];
+    a.out[cc * a.osc + j * a.osj] = sum;
+}
+
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(RedArgs a) {
+    reduce_splits(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 struct GradArgs {
-    const uint16_t *V;  // [M][C] (ldv)
+    const uint16_t *V;  // BF16 V [M][C] (ldv), or
     int64_t ldv;
-    const uint16_t *T;  // [M][ldt], ranks j < r
+    const uint8_t *vc, *vs;  // NVFP4 V: codes [M][C/2], scales [M][C/16], row scales [M]
+    const float *vd;
+    const uint16_t *T;  // [M][ldt], ranks j < r (zero for r <= j < ldt)
     int64_t ldt;
     int M, C, r;
-    int mchunk;   // tokens per workgroup (a multiple of 64)
-    float *part;  // [msplit][C][32 JT]
+    int mchunk;   // tokens per workgroup (a multiple of kGradMT)
+    int cblocks;  // column blocks; workgroup b < cblocks * msplit: block b % cblocks, split b / cblocks
+    float *part;  // [msplit][C][32 JT] FP32 partials
+    RedArgs side;  // workgroups past the contraction's reduce an earlier contraction's partials
 };
 
-constexpr int kGradWaves = 4;
-constexpr int kGradU = 4;  // K16 steps whose loads are in flight together
+constexpr int kGradMT = 64;  // tokens per LDS stage
 
-// 8 BF16 values at p, p + ld, ..., p + 7 ld (rows at or past mlim read as 0).
-__device__ __forceinline__ bf16x8_t gather8(const uint16_t *p, int64_t ld, int m, int mlim, bool ok) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = (ok && m + 2 * q < mlim) ? p[(int64_t)(2 * q) * ld] : 0u;
-        const uint32_t hi = (ok && m + 2 * q + 1 < mlim) ? p[(int64_t)(2 * q + 1) * ld] : 0u;
-        w[q] = lo | (hi << 16);
-    }
-    return __builtin_bit_cast(bf16x8_t, u32x4{w[0], w[1], w[2], w[3]});
-}
-
-template <int JT>
+// Both gradients contract over the tokens: out[c][j] = sum_m V[m][c] T[m][j].
+// A workgroup of 4 wavefronts owns CB columns (each wavefront CB / 4, as
+// 32-column MFMA tiles, v_mfma_f32_32x32x16_bf16 with D = out) and a token
+// range in stages of 64 tokens: V [64][CB] and T [64][32 JT] are loaded with
+// 16-byte row-contiguous loads (NVFP4 V: 16 code bytes, two scale bytes and
+// the row scale per 32 columns, decoded to BF16), stored in LDS and read back
+// as MFMA operands (lane (h, l) takes 8 consecutive tokens 8h.. of column or
+// rank l).  The next stage's loads are issued before the current stage's
+// MFMAs.  The token ranges (splits) of a column block give FP32 partials that
+// a reduction sums in split order, so every run adds in the same order.  Loads
+// past M or C read a clamped address and are zeroed.
+template <int CB, int JT, bool NV>
 __global__ __launch_bounds__(256) void lora_grad_kernel(GradArgs g) {
-    __shared__ float red[kGradWaves][JT][16][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int MT = kGradMT;
+    constexpr int VS = CB + 8;  // LDS row strides (BF16 elements)
+    constexpr int TW = 32 * JT;
+    constexpr int TS = TW + 8;
+    constexpr int CT = CB / 128;  // 32-column tiles per wavefront
+    constexpr int VP = NV ? MT * CB / 32 / 256 : MT * CB / 8 / 256;  // per thread: 32-column parts or 16-byte pieces
+    static_assert(VP >= 1 && MT * TW / 8 == 256 * JT, "staging covers the tiles");
+    __shared__ uint16_t Vs[MT * VS];
+    __shared__ uint16_t Ts[MT * TS];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nwg = g.cblocks * ((g.M + g.mchunk - 1) / g.mchunk);
+    if ((int)blockIdx.x >= nwg) {  // side workgroup (uniform, before any barrier)
+        reduce_splits(g.side, (int64_t)(blockIdx.x - nwg) * 256 + tid);
+        return;
+    }
+    const int split = (int)blockIdx.x / g.cblocks;
     const int h = lane >> 5, l = lane & 31;
-    const int c0 = blockIdx.x * 32;
-    const int c = c0 + l;
-    const bool cok = c < g.C;
-    const int wchunk = g.mchunk / kGradWaves;  // a multiple of 16
-    const int mb = blockIdx.y * g.mchunk + w * wchunk;
-    const int me = min(g.M, mb + wchunk);
-    float16_t acc[JT];
+    const int c0 = ((int)blockIdx.x % g.cblocks) * CB;
+    const int mb = split * g.mchunk, me = min(g.M, mb + g.mchunk);
+    const bool c32 = (g.C & 31) == 0;
+    u32x4 rv[VP];
+    uint32_t rs[NV ? VP : 1];
+    float rd[NV ? VP : 1];
+    u32x4 rt[JT];
+    auto gload = [&](int m0) {
 #pragma unroll
-    for (int t = 0; t < JT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-    for (int m0 = mb; m0 < me; m0 += 16 * kGradU) {
-        bf16x8_t va[kGradU], vb[kGradU][JT];
-#pragma unroll
-        for (int u = 0; u < kGradU; ++u) {
-            const int m = m0 + 16 * u + 8 * h;
-            va[u] = gather8(g.V + (int64_t)m * g.ldv + c, g.ldv, m, me, cok);
-#pragma unroll
-            for (int t = 0; t < JT; ++t) {
-                const int j = 32 * t + l;
-                vb[u][t] = gather8(g.T + (int64_t)m * g.ldt + j, g.ldt, m, me, j < g.r);
+        for (int i = 0; i < VP; ++i) {
+            const int p = tid + 256 * i;
+            if (NV) {
+                const int row = p / (CB / 32), col = c0 + 32 * (p % (CB / 32));
+                const int m = min(m0 + row, g.M - 1);
+                const bool ok = m0 + row < me && col < g.C;
+                const int cl = ok ? col : 0;
+                const uint8_t *cr = g.vc + (int64_t)m * (g.C / 2) + cl / 2;
+                const uint8_t *sr = g.vs + (int64_t)m * (g.C / 16) + cl / 16;
+                uint32_t s2;
+                if (c32) {
+                    rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cr));
+                    s2 = *reinterpret_cast<const uint16_t *>(sr);
+                } else {
+                    const bool two = cl + 16 < g.C;
+                    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(cr));
+                    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr));
+                    rv[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    s2 = (uint32_t)sr[0] | ((uint32_t)sr[two ? 1 : 0] << 8);
+                }
+                if (!ok) s2 = 0u;
+                else if (col + 16 >= g.C) s2 &= 0xFFu;
+                rs[i] = s2;
+                rd[i] = g.vd[m];
+            } else {
+                const int row = p / (CB / 8), col = c0 + 8 * (p % (CB / 8));
+                const int m = min(m0 + row, g.M - 1);
+                const bool ok = m0 + row < me && col < g.C;
+                const u32x4 v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(g.V + (int64_t)m * g.ldv + (ok ? col : 0)));
+                rv[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
-        for (int u = 0; u < kGradU; ++u)
+        for (int i = 0; i < JT; ++i) {
+            const int p = tid + 256 * i;
+            const int row = p / (TW / 8), col = 8 * (p % (TW / 8));
+            const int m = min(m0 + row, g.M - 1);
+            const bool ok = m0 + row < me && col < g.ldt;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(g.T + (int64_t)m * g.ldt + (ok ? col : 0));
+            rt[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto lstore = [&]() {
 #pragma unroll
-            for (int t = 0; t < JT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[u], vb[u][t], acc[t], 0, 0, 0);
+        for (int i = 0; i < VP; ++i) {
+            const int p = tid + 256 * i;
+            if (NV) {
+                const int row = p / (CB / 32), cc = 32 * (p % (CB / 32));
+                const half2_t s0 = e4m3_to_h2(rs[i] & 0xFFu), s1 = e4m3_to_h2(rs[i] >> 8);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(&Vs[row * VS + cc]);
+                dst[0] = dequant8_bf16(rv[i].x, s0, rd[i]);
+                dst[1] = dequant8_bf16(rv[i].y, s0, rd[i]);
+                dst[2] = dequant8_bf16(rv[i].z, s1, rd[i]);
+                dst[3] = dequant8_bf16(rv[i].w, s1, rd[i]);
+            } else {
+                const int row = p / (CB / 8), cc = 8 * (p % (CB / 8));
+                *reinterpret_cast<u32x4 *>(&Vs[row * VS + cc]) = rv[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < JT; ++i) {
+            const int p = tid + 256 * i;
+            const int row = p / (TW / 8), col = 8 * (p % (TW / 8));
+            *reinterpret_cast<u32x4 *>(&Ts[row * TS + col]) = rt[i];
+        }
+    };
+    // 8 BF16 values at LDS rows r0 + 8h .. r0 + 8h + 7 of column col (stride S)
+    auto col8 = [&](const uint16_t *base, int S, int r0, int col) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            wv[q] = (uint32_t)base[(r0 + 8 * h + 2 * q) * S + col] |
+                    ((uint32_t)base[(r0 + 8 * h + 2 * q + 1) * S + col] << 16);
+        return __builtin_bit_cast(bf16x8_t, u32x4{wv[0], wv[1], wv[2], wv[3]});
+    };
+    float16_t acc[CT][JT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t = 0; t < JT; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[ct][t][e] = 0.0f;
+    if (mb < me) {
+        gload(mb);
+        for (int m0 = mb; m0 < me; m0 += MT) {
+            __syncthreads();  // the previous stage's LDS reads are done
+            lstore();
+            if (m0 + MT < me) gload(m0 + MT);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < MT / 16; ++s) {
+                bf16x8_t b[JT];
+#pragma unroll
+                for (int t = 0; t < JT; ++t) b[t] = col8(Ts, TS, 16 * s, 32 * t + l);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const bf16x8_t a = col8(Vs, VS, 16 * s, (CB / 4) * w + 32 * ct + l);
+#pragma unroll
+                    for (int t = 0; t < JT; ++t)
+                        acc[ct][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t], acc[ct][t], 0, 0, 0);
+                }
+            }
+        }
     }
-    // accumulator element e of lane (h, l): column c0 + 8 (e / 4) + 4 h + e % 4, rank 32 t + l
+    // accumulator element e of lane (h, l): column 8 (e / 4) + 4 h + e % 4 of the tile, rank 32 t + l
+    float *dst = g.part + (int64_t)split * g.C * TW;
 #pragma unroll
-    for (int t = 0; t < JT; ++t)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[w][t][e][lane] = acc[t][e];
-    __syncthreads();
-    float *dst = g.part + (int64_t)blockIdx.y * g.C * (32 * JT);
-    for (int i = threadIdx.x; i < JT * 16 * 64; i += 256) {
-        const int t = i / (16 * 64), e = (i / 64) % 16, ln = i % 64;
-        float sum = red[0][t][e][ln];
+        for (int t = 0; t < JT; ++t)
 #pragma unroll
-        for (int q = 1; q < kGradWaves; ++q) sum += red[q][t][e][ln];
-        const int cc = c0 + 8 * (e >> 2) + 4 * (ln >> 5) + (e & 3);
-        const int j = 32 * t + (ln & 31);
-        if (cc < g.C) dst[(int64_t)cc * (32 * JT) + j] = sum;
-    }
-}
-
-// out[c * osc + j * osj] = sum over splits s (in order) of part[s][c][j], j < r.
-__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(const float *part, int msplit, int C, int r, int jw,
-                                                               float *out, int64_t osc, int64_t osj) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)C * r) return;
-    const int cc = (int)(i / r), j = (int)(i % r);
-    float sum = 0.0f;
-    for (int s = 0; s < msplit; ++s) sum += part[((int64_t)s * C + cc) * jw + j];
-    out[cc * osc + j * osj] = sum;
+            for (int e = 0; e < 16; ++e) {
+                const int cc = c0 + (CB / 4) * w + 32 * ct + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (cc < g.C) dst[(int64_t)cc * TW + 32 * t + l] = acc[ct][t][e];
+            }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, int64_t n) {
@@ -139,19 +226,24 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, int64_t n) {
 }
 
 struct GradPlan {
-    int msplit, mchunk;
+    int cb, msplit, mchunk;
 };
 
+// CB = 256 columns for wide outputs (the rank operand is re-read once per
+// column block), 128 otherwise; token splits for about 512 workgroups, with at
+// least 4 stages per workgroup and at most kMaxSplits.
 static GradPlan grad_plan(int64_t M, int64_t C) {
-    const int64_t cblocks = (C + 31) / 32;
-    int64_t ms = (1024 + cblocks - 1) / cblocks;  // about 1024 workgroups
-    const int64_t max_ms = (M + 255) / 256;          // at least 64 tokens per wavefront
+    const int cb = C >= 4096 ? 256 : 128;
+    const int64_t cblocks = (C + cb - 1) / cb;
+    int64_t ms = (512 + cblocks - 1) / cblocks;
+    int64_t max_ms = (M + 4 * kGradMT - 1) / (4 * kGradMT);
+    if (max_ms > kMaxSplits) max_ms = kMaxSplits;
     if (ms > max_ms) ms = max_ms;
     if (ms < 1) ms = 1;
     int64_t mchunk = (M + ms - 1) / ms;
-    mchunk = (mchunk + 63) / 64 * 64;
+    mchunk = (mchunk + kGradMT - 1) / kGradMT * kGradMT;
     ms = (M + mchunk - 1) / mchunk;
-    return {(int)(ms > 0 ? ms : 1), (int)mchunk};
+    return {cb, (int)(ms > 0 ? ms : 1), (int)mchunk};
 }
 
 static size_t grad_part_bytes(int64_t M, int64_t C, int r) {
@@ -160,29 +252,41 @@ static size_t grad_part_bytes(int64_t M, int64_t C, int r) {
     return (size_t)round_up((int64_t)p.msplit * C * 32 * jt * 4, 256);
 }
 
+// Workspace: T^ and T' [M][rpad] BF16, B^T [r][N] BF16, the FP32 partials of
+// both contractions (dB's are reduced during dA's contraction).
 static size_t lora_grads_ws(int64_t M, int64_t N, int64_t K, int r) {
     const int64_t rpad = round_up(r, 16);
-    const size_t xh = (size_t)round_up(M * K * 2, 256);
     const size_t t = (size_t)round_up(M * rpad * 2, 256);
-    const size_t pn = grad_part_bytes(M, N, r), pk = grad_part_bytes(M, K, r);
-    return xh + 2 * t + (pn > pk ? pn : pk);
+    const size_t bt = (size_t)round_up((int64_t)r * N * 2, 256);
+    return 2 * t + bt + grad_part_bytes(M, N, r) + grad_part_bytes(M, K, r);
 }
 
-static pact_status launch_grad(const uint16_t *V, int64_t ldv, const uint16_t *T, int64_t ldt, int M, int C, int r,
-                               float *part, float *out, int64_t osc, int64_t osj, hipStream_t st) {
-    const GradPlan p = grad_plan(M, C);
-    const int jt = (r + 31) / 32;
-    GradArgs g = {V, ldv, T, ldt, M, C, r, p.mchunk, part};
-    const dim3 grid((unsigned)((C + 31) / 32), (unsigned)p.msplit);
-    if (jt == 1)
-        hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(256), 0, st, g);
-    else
-        hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(256), 0, st, g);
-    PACT_TRY(launch_status());
-    const int64_t n = (int64_t)C * r;
-    hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, p.msplit,
-                       C, r, 32 * jt, out, osc, osj);
-    return launch_status();
+template <bool NV>
+static void launch_grad_kernel(const GradArgs &g, const GradPlan &p, int jt, hipStream_t st) {
+    const dim3 grid((unsigned)(g.cblocks * p.msplit + g.side.wgs));
+    if (p.cb == 256) {
+        if (jt == 1) hipLaunchKernelGGL((lora_grad_kernel<256, 1, NV>), grid, dim3(256), 0, st, g);
+        else hipLaunchKernelGGL((lora_grad_kernel<256, 2, NV>), grid, dim3(256), 0, st, g);
+    } else {
+        if (jt == 1) hipLaunchKernelGGL((lora_grad_kernel<128, 1, NV>), grid, dim3(256), 0, st, g);
+        else hipLaunchKernelGGL((lora_grad_kernel<128, 2, NV>), grid, dim3(256), 0, st, g);
+    }
+}
+
+// Partials of V^T T over the tokens (V BF16 when g.vc is null, else NVFP4),
+// plus g.side's reduction in extra workgroups; returns the reduction of this
+// contraction's partials into out[c * osc + j * osj].
+static RedArgs launch_grad(GradArgs g, float *out, int64_t osc, int64_t osj, hipStream_t st, pact_status *status) {
+    const GradPlan p = grad_plan(g.M, g.C);
+    const int jt = (g.r + 31) / 32;
+    g.mchunk = p.mchunk;
+    g.cblocks = (g.C + p.cb - 1) / p.cb;
+    if (g.vc) launch_grad_kernel<true>(g, p, jt, st);
+    else launch_grad_kernel<false>(g, p, jt, st);
+    *status = launch_status();
+    RedArgs red{g.part, p.msplit, g.C, g.r, 32 * jt, out, osc, osj, 0};
+    red.wgs = (int)(((int64_t)g.C * g.r + 255) / 256);
+    return red;
 }
 
 }  // namespace pact
@@ -219,22 +323,65 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     if (!aligned16(ws)) return PACT_ERR_MISALIGNED;
     const int rpad = (int)round_up(r, 16);
     uint8_t *base = static_cast<uint8_t *>(ws);
-    uint16_t *Xh = reinterpret_cast<uint16_t *>(base);
-    base += round_up(M * K * 2, 256);
     uint16_t *Th = reinterpret_cast<uint16_t *>(base);
     base += round_up(M * rpad * 2, 256);
     uint16_t *Tp = reinterpret_cast<uint16_t *>(base);
     base += round_up(M * rpad * 2, 256);
-    float *part = reinterpret_cast<float *>(base);
-    // X^ = bf16(deq(Xq))
-    const int64_t blocks = M * (K / 16);
-    hipLaunchKernelGGL(dequant_bf16_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, st, Xq->codes,
-                       Xq->scales, Xq->row_scale, M, (int)K, Xh);
-    PACT_TRY(launch_status());
-    // T^ = bf16(s X^ A^T): P(j, k) = A[j K + k];  T' = bf16(s dY B): P(j, n) = B[n r + j]
-    PACT_TRY(launch_lora_down(DownArgs{Xh, K, (int)M, (int)K, lora->A, K, 1, r, rpad, 0, lora->scale, Th}, st));
-    PACT_TRY(launch_lora_down(DownArgs{dY, ld_dy, (int)M, (int)N, lora->B, 1, r, r, rpad, 0, lora->scale, Tp}, st));
-    // dB[n][j] = sum_m dY[m][n] T^[m][j];  dA[j][k] = sum_m T'[m][j] X^[m][k]
-    PACT_TRY(launch_grad(dY, ld_dy, Th, rpad, (int)M, (int)N, r, part, dB, r, 1, st));
-    return launch_grad(Xh, K, Tp, rpad, (int)M, (int)K, r, part, dA, 1, K, st);
+    uint16_t *Bt = reinterpret_cast<uint16_t *>(base);
+    base += round_up((int64_t)r * N * 2, 256);
+    float *partB = reinterpret_cast<float *>(base);
+    float *partA = reinterpret_cast<float *>(base + grad_part_bytes(M, N, r));
+    // T^ = bf16(s X^ A^T) straight from the NVFP4 rows (P(j, k) = A[j K + k]);
+    // its side workgroups write B^T
+    DownArgs dh{};
+    dh.ldx = K;
+    dh.M = (int)M;
+    dh.Kl = (int)K;
+    dh.Ps = lora->A;
+    dh.p_sj = K;
+    dh.p_sk = 1;
+    dh.r = r;
+    dh.rpad = rpad;
+    dh.scale = lora->scale;
+    dh.T = Th;
+    dh.xc = Xq->codes;
+    dh.xs = Xq->scales;
+    dh.xd = Xq->row_scale;
+    dh.side_B = lora->B;
+    dh.side_Bt = Bt;
+    dh.side_N = (int)N;
+    dh.side_r = r;
+    dh.side_wgs = (int)((N * r + 255) / 256);
+    PACT_TRY(launch_lora_down_nvfp4(dh, st));
+    // T' = bf16(s dY B): P(j, n) = B^T[j N + n]
+    PACT_TRY(launch_lora_down(DownArgs{dY, ld_dy, (int)M, (int)N, Bt, N, 1, r, rpad, 0, lora->scale, Tp}, st));
+    // dB[n][j] = sum_m dY[m][n] T^[m][j];  dA[j][k] = sum_m T'[m][j] X^[m][k];
+    // dB's split reduction runs beside dA's contraction, dA's on its own
+    pact_status stt = PACT_OK;
+    GradArgs gb{};
+    gb.V = dY;
+    gb.ldv = ld_dy;
+    gb.T = Th;
+    gb.ldt = rpad;
+    gb.M = (int)M;
+    gb.C = (int)N;
+    gb.r = r;
+    gb.part = partB;
+    const RedArgs redB = launch_grad(gb, dB, r, 1, st, &stt);
+    PACT_TRY(stt);
+    GradArgs ga{};
+    ga.vc = Xq->codes;
+    ga.vs = Xq->scales;
+    ga.vd = Xq->row_scale;
+    ga.T = Tp;
+    ga.ldt = rpad;
+    ga.M = (int)M;
+    ga.C = (int)K;
+    ga.r = r;
+    ga.part = partA;
+    ga.side = redB;
+    const RedArgs redA = launch_grad(ga, dA, 1, K, st, &stt);
+    PACT_TRY(stt);
+    hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)redA.wgs), dim3(256), 0, st, redA);
+    return launch_status();
 }

@@ -173,7 +173,7 @@ def test_lora_grads_validation(L):
     lo = pb.pact_lora(FAKE, FAKE, r, 2.0)
     f = L.pact_lora_grads_nvfp4
     need = L.pact_lora_grads_workspace(M, N, K, r)
-    assert need >= M * K * 2                                                  # holds X^ in BF16
+    assert need >= 2 * M * 16 * 2                                             # holds T^ and T'
     assert L.pact_lora_grads_workspace(M, N, K, 0) == 0
     assert f(ctypes.byref(q), FAKE, N, N, None, FAKE, FAKE, FAKE, need, None) == 1        # no adapter
     big = pb.pact_lora(FAKE, FAKE, 65, 2.0)
