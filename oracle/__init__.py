@@ -87,6 +87,8 @@ def lib():
         L.orc_dot_bf16_f32.argtypes = [P, P, I64]
         L.orc_rmsnorm_bwd.argtypes = [P, I64, P, P, P, P, P, P, I64, I64, I64, P, P, P, P]
         L.orc_lora_grads.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P, ctypes.c_int32, ctypes.c_float, P, P]
+        D = ctypes.c_double
+        L.orc_adamw_step.argtypes = [P, P, P, P, I64, D, D, D, D, D, I64]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -352,3 +354,23 @@ def lora_grads(xq: NVFP4, dY: np.ndarray, A: np.ndarray, B: np.ndarray, s: float
     lib().orc_lora_grads(_p(_c(xq.codes, np.uint8)), _p(_c(xq.scales, np.uint8)), _p(_c(xq.d, np.float32)),
                          M, K, _p(dY), N, N, _p(A), _p(B), r, float(s), _p(dA), _p(dB))
     return dA, dB
+
+
+# ---- optimizer --------------------------------------------------------------
+def adamw_step(p, m, v, g, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int):
+    """One AdamW step in binary64 on copies of (p, m, v); returns the new
+    (p, m, v) as float64 arrays."""
+    p = np.array(p, dtype=np.float64, copy=True).ravel()
+    m = np.array(m, dtype=np.float64, copy=True).ravel()
+    v = np.array(v, dtype=np.float64, copy=True).ravel()
+    g = np.ascontiguousarray(np.asarray(g, dtype=np.float64).ravel())
+    assert p.size == m.size == v.size == g.size
+    lib().orc_adamw_step(_p(p), _p(m), _p(v), _p(g), p.size, float(lr), float(beta1), float(beta2), float(eps),
+                         float(weight_decay), int(step))
+    return p, m, v
+
+
+def bf16_of_master(p) -> np.ndarray:
+    """BF16 bits of the FP32 master copy of p: bf16(fl32(p))."""
+    f = np.asarray(p, dtype=np.float64).astype(np.float32)
+    return np.array([lib().orc_f32_to_bf16(float(x)) for x in f.ravel()], dtype=np.uint16).reshape(f.shape)

@@ -738,3 +738,27 @@ void orc_lora_grads(const uint8_t *xc, const uint8_t *xs, const float *xd, int64
     free(Th);
     free(Tp);
 }
+
+/* ------------------------------------------------------------------------- */
+/* AdamW step of the trainable adapters.  The hotdry.top Unsloth post         */
+/* (section on paged optimizers) has Adam keep a first and a second moment    */
+/* per trainable parameter in 32-bit state; the update itself is the          */
+/* published AdamW rule (Loshchilov & Hutter, decoupled weight decay):        */
+/*   p <- p - lr wd p;  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;    */
+/*   p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).             */
+/* Binary64 throughout; t >= 1 is the step number.                            */
+/* ------------------------------------------------------------------------- */
+void orc_adamw_step(double *p, double *m, double *v, const double *g, int64_t n, double lr, double b1, double b2,
+                    double eps, double wd, int64_t t) {
+    assert(t >= 1);
+    const double bc1 = 1.0 - pow(b1, (double)t);
+    const double bc2 = 1.0 - pow(b2, (double)t);
+    for (int64_t i = 0; i < n; ++i) {
+        p[i] = p[i] - lr * wd * p[i];
+        m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+        v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+        const double mhat = m[i] / bc1;
+        const double vhat = v[i] / bc2;
+        p[i] = p[i] - lr * mhat / (sqrt(vhat) + eps);
+    }
+}
