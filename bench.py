@@ -80,7 +80,9 @@ def parse():
                     help="tokens in the oracle sample (0: the whole batch, at most 1024)")
     ap.add_argument("--lora-grads", action="store_true",
                     help="add the LoRA weight gradients (dA, dB of every projection, from the NVFP4 stash) "
-                         "to each layer's backward; timed as their own kind, never counted as frozen FLOPs")
+                         "to each layer's backward and one fused AdamW step over all adapters; timed as their "
+                         "own kinds, never counted as frozen FLOPs (under graph replay the AdamW step number "
+                         "is the captured one)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step without graph capture")
     ap.add_argument("--no-isolated", action="store_true",
@@ -119,6 +121,20 @@ class Stack:
         self.Wf, self.Wb, self.lora, self.g1, self.g2 = [], [], [], [], []
         self.layout_ms = 0.0
         st = torch.cuda.current_stream()
+        self.lora_grads = lora_grads
+        if lora_grads:
+            # every adapter of every layer lives in one flat buffer (BF16 copy for the GEMMs, FP32 master,
+            # moments and gradients), so one AdamW launch updates them all
+            r = shape.rank
+            sizes = [r * k + n * r for _ in range(layers) for n, k in shape.projections().values()]
+            self.n_params = sum(sizes)
+            self.wflat = torch.empty(self.n_params, dtype=torch.bfloat16, device=dev)
+            self.pflat = torch.empty(self.n_params, dtype=torch.float32, device=dev)
+            self.mflat = torch.zeros(self.n_params, dtype=torch.float32, device=dev)
+            self.vflat = torch.zeros(self.n_params, dtype=torch.float32, device=dev)
+            self.gflat = torch.zeros(self.n_params, dtype=torch.float32, device=dev)
+            self.gA, self.gB = [], []
+            off = 0
         for l in range(layers):
             li = synth.layer_inputs(shape, seed=seed, layer=l)
             if l == 0:
@@ -127,8 +143,27 @@ class Stack:
             Wbf = {n: self.bf(li.W[n]) for n in self.names}
             self.g1.append(self.bf(li.gamma1))
             self.g2.append(self.bf(li.gamma2))
-            self.lora.append({n: pb.LoRA(self.bf(li.A[n]), self.bf(li.B[n]), shape.lora_scale)
-                              for n in self.names})
+            if lora_grads:
+                lo, gA, gB = {}, {}, {}
+                for n in self.names:
+                    nn, kk = shape.projections()[n]
+                    r = shape.rank
+                    assert off % 8 == 0 and (r * kk) % 8 == 0
+                    A = self.wflat[off:off + r * kk].view(r, kk)
+                    A.copy_(self.bf(li.A[n]))
+                    gA[n] = self.gflat[off:off + r * kk].view(r, kk)
+                    off += r * kk
+                    B = self.wflat[off:off + nn * r].view(nn, r)
+                    B.copy_(self.bf(li.B[n]))
+                    gB[n] = self.gflat[off:off + nn * r].view(nn, r)
+                    off += nn * r
+                    lo[n] = pb.LoRA(A, B, shape.lora_scale)
+                self.lora.append(lo)
+                self.gA.append(gA)
+                self.gB.append(gB)
+            else:
+                self.lora.append({n: pb.LoRA(self.bf(li.A[n]), self.bf(li.B[n]), shape.lora_scale)
+                                  for n in self.names})
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
             lay = {n: pb.pact_build_weight_layouts(Wbf[n]) for n in self.names}
@@ -155,13 +190,10 @@ class Stack:
         self.dxs = [self.dout, E(M, H), E(M, H)]
         need = max(pb.pact_gemm_workspace(M, n, k, shape.rank) for n, k in shape.projections().values())
         self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
-        self.lora_grads = lora_grads
-        if lora_grads:  # one dA/dB pair per projection, overwritten by every layer
+        if lora_grads:
+            self.pflat.copy_(self.wflat.float())
+            self.adam_step = 0
             r = shape.rank
-            self.gA = {n: torch.empty((r, k), dtype=torch.float32, device=dev)
-                       for n, (_, k) in shape.projections().items()}
-            self.gB = {n: torch.empty((nn, r), dtype=torch.float32, device=dev)
-                       for n, (nn, _) in shape.projections().items()}
             gneed = max(pb.pact_lora_grads_workspace(M, n, k, r) for n, k in shape.projections().values())
             self.gws = torch.empty((max(gneed, 16),), dtype=torch.uint8, device=dev)
 
@@ -174,14 +206,14 @@ class Stack:
         lora_fl = lambda n, k: 2 * M * r * (n + k)
         c = []
 
-        def grads(nm, xq, dY, L):
-            """dA, dB of projection nm (input xq from the stash, output gradient dY)."""
+        def grads(nm, xq, dY, L, l):
+            """dA, dB of projection nm of layer l (input xq from the stash, output gradient dY)."""
             if not self.lora_grads:
                 return
             n, k = S.projections()[nm]
-            c.append(("lora_grads", 0, nvb(M, k) + 2 * M * n + 4 * r * (n + k) + 4 * r * (n + k),
-                      lambda nm=nm, xq=xq, dY=dY, L=L: pb.pact_lora_grads_nvfp4(
-                          xq, dY, L[nm], dA=self.gA[nm], dB=self.gB[nm], ws=self.gws), 4 * M * r * (n + k)))
+            c.append(("lora_grads", 0, nvb(M, k) + 2 * M * n + 2 * r * (n + k) + 4 * r * (n + k),
+                      lambda nm=nm, xq=xq, dY=dY, L=L, l=l: pb.pact_lora_grads_nvfp4(
+                          xq, dY, L[nm], dA=self.gA[l][nm], dB=self.gB[l][nm], ws=self.gws), 4 * M * r * (n + k)))
         xin = lambda l: self.xs[0] if l == 0 else self.xs[1 + (l - 1) % 2]
         xout = lambda l: self.xs[1 + l % 2]
         for l in range(self.L):
@@ -221,22 +253,22 @@ class Stack:
                           lambda dout=dout: pb.pact_quantize_nvfp4(dout, self.doq), 0))
             c.append(("gemm_dgrad", gemm_fl(H, I), 0, lambda dout=dout, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.doq, Wb["down"], dY=dout, lora=L["down"], dX=self.dh, ws=ws), lora_fl(H, I)))
-            grads("down", st["hq"], dout, L)
+            grads("down", st["hq"], dout, L, l)
             c.append(("silu_mul_bwd", 0, M * I * 2 + 2 * nvb(M, I) + 2 * M * I * 2 + 2 * nvb(M, I),
                       lambda st=st: pb.pact_silu_mul_bwd_quant_nvfp4(self.dh, st["gq"], st["uq"], self.dg, self.du,
                                                                      self.dgq, self.duq), 0))
             c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dgq, Wb["gate"], dY=self.dg, lora=L["gate"], dX=self.dn, ws=ws), lora_fl(I, H)))
-            grads("gate", st["n2q"], self.dg, L)
+            grads("gate", st["n2q"], self.dg, L, l)
             c.append(("gemm_dgrad", gemm_fl(I, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.duq, Wb["up"], dY=self.du, lora=L["up"], C=self.dn, dX=self.dn, ws=ws), lora_fl(I, H)))
-            grads("up", st["n2q"], self.du, L)
+            grads("up", st["n2q"], self.du, L, l)
             c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2 + nvb(M, H),
                       lambda st=st, l=l, dout=dout: pb.pact_rmsnorm_bwd_nvfp4(
                           self.dn, st["n2q"], self.g2[l], st["rstd2"], C=dout, dx=self.dx2, dxq=self.dx2q), 0))
             c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dx2q, Wb["o"], dY=self.dx2, lora=L["o"], dX=self.da, ws=ws), lora_fl(H, H)))
-            grads("o", st["aq"], self.dx2, L)
+            grads("o", st["aq"], self.dx2, L, l)
             dq, dk, dv = self.da, self.da[:, :KV], self.da[:, KV:2 * KV]
             c.append(("quantize", 0, M * H * 2 + nvb(M, H), lambda dq=dq: pb.pact_quantize_nvfp4(dq, self.dqq), 0))
             c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dk=dk: pb.pact_quantize_nvfp4(dk, self.dkq), 0))
@@ -247,15 +279,21 @@ class Stack:
                 self.dkq, Wb["k"], dY=dk, lora=L["k"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
             c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dvq, Wb["v"], dY=dv, lora=L["v"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
-            grads("q", st["n1q"], dq, L)
-            grads("k", st["n1q"], dk, L)
-            grads("v", st["n1q"], dv, L)
+            grads("q", st["n1q"], dq, L, l)
+            grads("k", st["n1q"], dk, L, l)
+            grads("v", st["n1q"], dv, L, l)
             last = j == self.L - 1
             c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2
                       + (0 if last else nvb(M, H)),
                       lambda st=st, l=l, dx=dx, last=last: pb.pact_rmsnorm_bwd_nvfp4(
                           self.dn, st["n1q"], self.g1[l], st["rstd1"], C=self.dx2, dx=dx,
                           dxq=None if last else self.doq, want_q=not last), 0))
+        if self.lora_grads:
+            def adam():
+                self.adam_step += 1
+                pb.pact_adamw_step(self.pflat, self.mflat, self.vflat, self.gflat, self.wflat, lr=1e-4,
+                                   weight_decay=0.01, step=self.adam_step)
+            c.append(("adamw", 0, 30 * self.n_params, adam, 0))
         return c
 
     def stash_bytes(self):
@@ -273,7 +311,8 @@ class Stack:
                 "intermediate": S.inter, "kv": S.kv, "lora_rank": S.rank, "lora_scale": S.lora_scale,
                 "step": "forward + input-gradient backward of every layer, 7 frozen NVFP4 projections "
                         "per layer with BF16 LoRA, fused RMSNorm/SiLU quantizers"
-                        + (", plus the LoRA weight gradients of every projection" if self.lora_grads else ""),
+                        + (", plus the LoRA weight gradients of every projection and one AdamW step over all "
+                           "adapters" if self.lora_grads else ""),
                 "lora_grads": self.lora_grads}
 
 
@@ -401,7 +440,7 @@ def isolated_timing(torch, calls, reps=10):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream()
     out = {}
-    for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant", "silu_mul_bwd", "rmsnorm_bwd"):
+    for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant", "silu_mul_bwd", "rmsnorm_bwd", "adamw"):
         cs = [c for c in calls if c[0] == kind]
         if not cs:
             continue

@@ -232,6 +232,21 @@ pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int6
                                   const pact_lora *lora, float *dA, float *dB, void *ws,
                                   size_t ws_bytes, void *stream);
 
+/* One AdamW step of the trainable adapters over a flat buffer of n FP32
+ * parameters (hotdry.top Unsloth post, section on paged optimizers: Adam keeps
+ * a first and a second moment per trainable parameter, in 32-bit state; the
+ * rule is AdamW with decoupled weight decay, Loshchilov & Hutter).  In place:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   p <- p - lr/(1 - b1^step) . m / (sqrt(v)/sqrt(1 - b2^step) + eps);
+ *   w <- bf16(p)   (the BF16 copy the GEMMs read; w may be NULL),
+ * in binary32 per element (the coefficients computed on the host in binary64
+ * and rounded once).  p, m, v, g, w: device buffers of n elements, 16-byte
+ * aligned; g is typically the gradients written by pact_lora_grads_nvfp4 into
+ * views of one flat buffer.  step >= 1, 0 <= beta < 1, lr, eps, wd >= 0 and
+ * finite, else PACT_ERR_INVALID_ARG.  n == 0 does nothing. */
+pact_status pact_adamw_step(float *p, float *m, float *v, const float *g, uint16_t *w, int64_t n, float lr,
+                            float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream);
+
 /* Diagnostic: out[i] = sigma32(g[i]) (the binary32 sigmoid-times-input the
  * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
  * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */

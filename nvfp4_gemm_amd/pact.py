@@ -40,7 +40,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
-           "pact_lora_grads_nvfp4"]
+           "pact_lora_grads_nvfp4", "pact_adamw_step"]
 
 
 class PactError(RuntimeError):
@@ -89,6 +89,8 @@ def lib():
         L.pact_lora_grads_workspace.argtypes = [I64, I64, I64, ctypes.c_int32]
         L.pact_lora_grads_nvfp4.restype = st
         L.pact_lora_grads_nvfp4.argtypes = [NV, P, I64, I64, LO, P, P, P, ctypes.c_size_t, P]
+        L.pact_adamw_step.restype = st
+        L.pact_adamw_step.argtypes = [P, P, P, P, P, I64, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, I64, P]
         L.pact_debug_dsilu32.restype = st
         L.pact_debug_dsilu32.argtypes = [P, P, I64, P]
         L.pact_debug_gemm_plan.restype = st
@@ -337,6 +339,17 @@ def pact_lora_grads_nvfp4(Xq: NVFP4Tensor, dY, lora: LoRA, dA=None, dB=None, ws=
     _check(lib().pact_lora_grads_nvfp4(ctypes.byref(dx), _ptr(dY), _ld(dY), N, ctypes.byref(dl), _ptr(dA),
                                        _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)), "pact_lora_grads_nvfp4")
     return dA, dB
+
+
+def pact_adamw_step(p, m, v, g, w=None, *, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                    weight_decay: float = 0.0, step: int, stream=None):
+    """In-place AdamW step over flat FP32 tensors p, m, v with gradient g;
+    writes bf16(p) into w when given."""
+    n = p.numel()
+    assert m.numel() == n and v.numel() == n and g.numel() == n and (w is None or w.numel() == n)
+    _check(lib().pact_adamw_step(_ptr(p), _ptr(m), _ptr(v), _ptr(g), _ptr(w) if w is not None else None, n,
+                                 float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+                                 _stream(stream)), "pact_adamw_step")
 
 
 def pact_debug_dsilu32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:

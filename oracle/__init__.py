@@ -89,6 +89,7 @@ def lib():
         L.orc_lora_grads.argtypes = [P, P, P, I64, I64, P, I64, I64, P, P, ctypes.c_int32, ctypes.c_float, P, P]
         D = ctypes.c_double
         L.orc_adamw_step.argtypes = [P, P, P, P, I64, D, D, D, D, D, I64]
+        L.orc_master_bf16.argtypes = [P, I64, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -372,5 +373,7 @@ def adamw_step(p, m, v, g, lr: float, beta1: float, beta2: float, eps: float, we
 
 def bf16_of_master(p) -> np.ndarray:
     """BF16 bits of the FP32 master copy of p: bf16(fl32(p))."""
-    f = np.asarray(p, dtype=np.float64).astype(np.float32)
-    return np.array([lib().orc_f32_to_bf16(float(x)) for x in f.ravel()], dtype=np.uint16).reshape(f.shape)
+    x = np.ascontiguousarray(np.asarray(p, dtype=np.float64))
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_master_bf16(_p(x), x.size, _p(out))
+    return out

@@ -748,6 +748,11 @@ void orc_lora_grads(const uint8_t *xc, const uint8_t *xs, const float *xd, int64
 /*   p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).             */
 /* Binary64 throughout; t >= 1 is the step number.                            */
 /* ------------------------------------------------------------------------- */
+/* BF16 of the binary32 master copy of binary64 values: bf16(fl32(x)). */
+void orc_master_bf16(const double *x, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16((float)x[i]);
+}
+
 void orc_adamw_step(double *p, double *m, double *v, const double *g, int64_t n, double lr, double b1, double b2,
                     double eps, double wd, int64_t t) {
     assert(t >= 1);

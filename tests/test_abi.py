@@ -182,3 +182,19 @@ def test_lora_grads_validation(L):
     assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE + 4, FAKE, FAKE, need, None) == 3  # dA
     assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need - 1, None) == 4  # workspace
     assert f(ctypes.byref(q), FAKE, N - 8, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need, None) == 1  # ld < N
+
+
+def test_adamw_validation(L):
+    """Argument checks of the AdamW entry point (host only)."""
+    f = L.pact_adamw_step
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.1)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, *hp, 1, None) == 0          # nothing to do
+    assert f(None, None, None, None, None, 0, *hp, 1, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, *hp, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 16, *hp, 0, None) == 1         # step counts from 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 1.0, 0.999, 1e-8, 0.1, 1, None) == 1   # beta1 = 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 16, -1e-3, 0.9, 0.999, 1e-8, 0.1, 1, None) == 1  # lr < 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 16, float("nan"), 0.9, 0.999, 1e-8, 0.1, 1, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 16, *hp, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE + 4, FAKE, 16, *hp, 1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 8, 16, *hp, 1, None) == 3
