@@ -65,7 +65,7 @@ GEMM_SOURCE = os.path.join(ROOT, "nvfp4_gemm_amd", "csrc", "pact_gemm.hip")
 CONFIGS = ["single_linear", "llama1b_layer", "qwen1.5b_layer", "llama3b_layer", "llama3b_stack28"]
 # kernels of the GEMM entry points: LoRA-down, one main kernel, and (split K)
 # the epilogue kernel; the main kernel's name marks one entry-point call
-GEMM_KERNELS = ("gemm_kernel", "gemm8_kernel", "lora_down_kernel", "splitk_epi_kernel")
+GEMM_KERNELS = ("gemm_kernel", "gemm8_kernel", "lora_down_kernel", "lora_down_pipe_kernel", "splitk_epi_kernel")
 GEMM_MAIN_KERNELS = ("gemm_kernel", "gemm8_kernel")
 
 
