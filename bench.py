@@ -6,10 +6,11 @@ backward (simolm.com PACT blog post, section "Method"; arXiv abstract of
 
 One step of a layer (every call goes through the C ABI):
   forward:  n1, n1q, rstd1 = rmsnorm_quant(x)
-            q, k, v = fwd GEMMs on n1q (+ LoRA on n1)
+            [q | k | v] = one grouped fwd GEMM on n1q over the concatenated
+            weight rows (+ block-diagonal LoRA on n1)
             a := q (the attention core is not part of the frozen path: identity
             stand-in), aq = Q(a), x2 = fwd_o(aq, a, C = x)
-            n2, n2q, rstd2 = rmsnorm_quant(x2); g, u = fwd GEMMs on n2q
+            n2, n2q, rstd2 = rmsnorm_quant(x2); [g | u] = one grouped fwd GEMM on n2q
             h, hq, gq, uq = silu_mul_quant(g, u); x' = fwd_down(hq, h, C = x2)
   backward: dh = dgrad_down(Q(dx'), dx')
             dg, du, dgq, duq = silu_mul_bwd(dh, gq, uq)          (from the stash)
@@ -83,6 +84,8 @@ def parse():
                          "to each layer's backward and one fused AdamW step over all adapters; timed as their "
                          "own kinds, never counted as frozen FLOPs (under graph replay the AdamW step number "
                          "is the captured one)")
+    ap.add_argument("--ungrouped", action="store_true",
+                    help="run q, k, v and gate, up as separate forward GEMMs (one call per projection)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step without graph capture")
     ap.add_argument("--no-isolated", action="store_true",
@@ -105,7 +108,7 @@ def nvb(rows, cols):
 class Stack:
     """Device buffers, weights and the step schedule of `layers` decoder layers."""
 
-    def __init__(self, shape, seed, layers, lora_grads=False):
+    def __init__(self, shape, seed, layers, lora_grads=False, grouped=True):
         import torch
         from nvfp4_gemm_amd import pact as pb
         from nvfp4_gemm_amd import synth
@@ -122,6 +125,7 @@ class Stack:
         self.layout_ms = 0.0
         st = torch.cuda.current_stream()
         self.lora_grads = lora_grads
+        self.grouped = grouped
         if lora_grads:
             # every adapter of every layer lives in one flat buffer (BF16 copy for the GEMMs, FP32 master,
             # moments and gradients), so one AdamW launch updates them all
@@ -170,7 +174,13 @@ class Stack:
             e1.record(st)
             torch.cuda.synchronize()
             self.layout_ms += e0.elapsed_time(e1)
-            self.Wf.append({n: lay[n][0] for n in self.names})
+            # forward layouts of projections that share an input, concatenated for the grouped GEMMs
+            if grouped:
+                self.Wf.append({"qkv": pb.NVFP4Tensor.cat_rows([lay[n][0] for n in ("q", "k", "v")]),
+                                "gu": pb.NVFP4Tensor.cat_rows([lay[n][0] for n in ("gate", "up")]),
+                                "o": lay["o"][0], "down": lay["down"][0]})
+            else:
+                self.Wf.append({n: lay[n][0] for n in self.names})
             self.Wb.append({n: lay[n][1] for n in self.names})
             del Wbf, lay
         # per-layer stash (kept from the forward to the backward)
@@ -179,16 +189,20 @@ class Stack:
                       for _ in range(layers)]
         # transient activations, shared by the layers
         self.xs = [self.x0, E(M, H), E(M, H)]    # layer input / output ping-pong (x0 is kept)
-        self.n1, self.q, self.k, self.v = E(M, H), E(M, H), E(M, KV), E(M, KV)
+        self.n1, self.qkv = E(M, H), E(M, H + 2 * KV)
+        self.q, self.k, self.v = self.qkv[:, :H], self.qkv[:, H:H + KV], self.qkv[:, H + KV:]
         self.x2, self.n2 = E(M, H), E(M, H)
-        self.gt, self.up, self.h = E(M, I), E(M, I), E(M, I)
+        self.gu, self.h = E(M, 2 * I), E(M, I)
+        self.gt, self.up = self.gu[:, :I], self.gu[:, I:]
         self.doq, self.dh = Q(M, H), E(M, I)
         self.dg, self.du, self.dgq, self.duq = E(M, I), E(M, I), Q(M, I), Q(M, I)
         self.dn = E(M, H)                        # gradient of a norm output (n2, then n1)
         self.dx2, self.dx2q, self.da = E(M, H), Q(M, H), E(M, H)
         self.dqq, self.dkq, self.dvq = Q(M, H), Q(M, KV), Q(M, KV)
         self.dxs = [self.dout, E(M, H), E(M, H)]
-        need = max(pb.pact_gemm_workspace(M, n, k, shape.rank) for n, k in shape.projections().values())
+        rpad = (shape.rank + 15) // 16 * 16
+        need = max([pb.pact_gemm_workspace(M, n, k, shape.rank) for n, k in shape.projections().values()]
+                   + [pb.pact_gemm_workspace(M, H + 2 * KV, H, 3 * rpad), pb.pact_gemm_workspace(M, 2 * I, H, 2 * rpad)])
         self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
         if lora_grads:
             self.pflat.copy_(self.wflat.float())
@@ -222,11 +236,16 @@ class Stack:
             c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
                       lambda x=x, st=st, l=l: pb.pact_rmsnorm_quant_nvfp4(x, self.g1[l], S.eps, self.n1,
                                                                           st["n1q"], st["rstd1"]), 0))
-            for nm, out in (("q", self.q), ("k", self.k), ("v", self.v)):
-                n, k = S.projections()[nm]
-                c.append(("gemm_fwd", gemm_fl(n, k), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
-                          pb.pact_gemm_nvfp4_fwd(st["n1q"], Wf[nm], X=self.n1, lora=L[nm], Y=out, ws=ws)),
-                          lora_fl(n, k)))
+            if self.grouped:  # q, k, v: one grouped GEMM over the concatenated weight rows (block-diagonal LoRA)
+                c.append(("gemm_fwd", gemm_fl(H + 2 * KV, H), 0, (lambda st=st, L=L, Wf=Wf: pb.pact_gemm_nvfp4_fwd_grouped(
+                    st["n1q"], Wf["qkv"], [H, KV, KV], X=self.n1, loras=[L["q"], L["k"], L["v"]], Y=self.qkv,
+                    ws=ws)), lora_fl(H, H) + 2 * lora_fl(KV, H)))
+            else:
+                for nm, out in (("q", self.q), ("k", self.k), ("v", self.v)):
+                    n, k = S.projections()[nm]
+                    c.append(("gemm_fwd", gemm_fl(n, k), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
+                              pb.pact_gemm_nvfp4_fwd(st["n1q"], Wf[nm], X=self.n1, lora=L[nm], Y=out, ws=ws)),
+                              lora_fl(n, k)))
             c.append(("quantize", 0, M * H * 2 + nvb(M, H),
                       lambda st=st: pb.pact_quantize_nvfp4(self.q, st["aq"]), 0))
             c.append(("gemm_fwd", gemm_fl(H, H), 0, lambda x=x, st=st, L=L, Wf=Wf: pb.pact_gemm_nvfp4_fwd(
@@ -234,10 +253,15 @@ class Stack:
             c.append(("rmsnorm_quant", 0, M * H * 2 * 2 + nvb(M, H) + 4 * M,
                       lambda st=st, l=l: pb.pact_rmsnorm_quant_nvfp4(self.x2, self.g2[l], S.eps, self.n2,
                                                                      st["n2q"], st["rstd2"]), 0))
-            for nm, out in (("gate", self.gt), ("up", self.up)):
-                c.append(("gemm_fwd", gemm_fl(I, H), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
-                          pb.pact_gemm_nvfp4_fwd(st["n2q"], Wf[nm], X=self.n2, lora=L[nm], Y=out, ws=ws)),
-                          lora_fl(I, H)))
+            if self.grouped:  # gate, up: one grouped GEMM
+                c.append(("gemm_fwd", gemm_fl(2 * I, H), 0, (lambda st=st, L=L, Wf=Wf: pb.pact_gemm_nvfp4_fwd_grouped(
+                    st["n2q"], Wf["gu"], [I, I], X=self.n2, loras=[L["gate"], L["up"]], Y=self.gu, ws=ws)),
+                    2 * lora_fl(I, H)))
+            else:
+                for nm, out in (("gate", self.gt), ("up", self.up)):
+                    c.append(("gemm_fwd", gemm_fl(I, H), 0, (lambda nm=nm, out=out, st=st, L=L, Wf=Wf:
+                              pb.pact_gemm_nvfp4_fwd(st["n2q"], Wf[nm], X=self.n2, lora=L[nm], Y=out, ws=ws)),
+                              lora_fl(I, H)))
             c.append(("silu_mul_quant", 0, M * I * 2 * 3 + 3 * nvb(M, I),
                       lambda st=st: pb.pact_silu_mul_quant_nvfp4(self.gt, self.up, self.h, st["hq"], st["gq"],
                                                                  st["uq"]), 0))
@@ -313,7 +337,8 @@ class Stack:
                         "per layer with BF16 LoRA, fused RMSNorm/SiLU quantizers"
                         + (", plus the LoRA weight gradients of every projection and one AdamW step over all "
                            "adapters" if self.lora_grads else ""),
-                "lora_grads": self.lora_grads}
+                "lora_grads": self.lora_grads,
+                "forward_gemms": "grouped q|k|v and gate|up" if self.grouped else "one per projection"}
 
 
 class Linear:
@@ -578,7 +603,7 @@ def main():
         work = Linear(args.seed)
     else:
         shape = synth.LAYERS[args.config]
-        work = Stack(shape, args.seed, shape.layers, lora_grads=args.lora_grads)
+        work = Stack(shape, args.seed, shape.layers, lora_grads=args.lora_grads, grouped=not args.ungrouped)
     st = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     calls = work.calls()

@@ -170,6 +170,24 @@ pact_status pact_gemm_nvfp4_fwd(const pact_nvfp4 *Xq, const uint16_t *X, int64_t
                                 const uint16_t *C, uint16_t *Y, int64_t ld_y,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* Grouped forward of ngroups (1..4) projections that share their input, such
+ * as q, k, v or gate, up (blog "Method", first bullet and closing
+ * paragraph: the same frozen NVFP4 GEMM and BF16 LoRA term per projection), as one GEMM
+ * over the concatenation of their weight rows:
+ *   Y[:, cols of g] = bf16( d_x d_w (Xq . W_g^T) + (bf16(s X A_g^T) B_g^T) ),
+ * the LoRA term block-diagonal (one LoRA-down over the concatenated ranks).
+ * W_fwd [sum N_g][K] NVFP4 holds W_0, W_1, ... row after row (e.g. each built
+ * by pact_build_weight_layouts into its slice); group_rows[g] = N_g (host
+ * array, multiples of 32); loras (host array of ngroups, or NULL: frozen only)
+ * with equal r and scale, A_g [r][K], B_g [N_g][r]; Y [M][sum N_g] (ld_y), no
+ * residual.  Workspace: pact_gemm_workspace(M, sum N_g, K, ngroups *
+ * round_up(r, 16)).  Each group's columns equal pact_gemm_nvfp4_fwd of that
+ * projection within the GEMM tolerance (the K-split plan may differ). */
+pact_status pact_gemm_nvfp4_fwd_grouped(const pact_nvfp4 *Xq, const uint16_t *X, int64_t ld_x,
+                                        const pact_nvfp4 *W_fwd, int32_t ngroups, const int64_t *group_rows,
+                                        const pact_lora *loras, uint16_t *Y, int64_t ld_y, void *ws,
+                                        size_t ws_bytes, void *stream);
+
 /* Input-gradient NVFP4 GEMM on the cached transposed layout (blog "Method",
  * first and fourth bullets):
  *   dX = bf16( d_dy[m] d_wb[k] (dYq . W_bwd^T)[m,k] + (bf16(s dY B) A)[m,k] (+ C[m,k]) )

@@ -50,6 +50,14 @@ struct GemmArgs {
     const uint16_t *Qs;  // LoRA-up operand: Q(n, j) = Qs[n * q_sn + j * q_sj], j < r
     int64_t q_sn, q_sj;
     int r, rpad;
+    int tld;  // row stride of T (rpad, or ngroups * rpad when grouped)
+    // grouped (block-diagonal) LoRA, ngroups > 1: output columns [gcol[g],
+    // gcol[g + 1]) use ranks [g rpad, g rpad + r) of T and Q(n, j) =
+    // Qg[g][(n - gcol[g]) q_sn + j] (q_sj == 1); group boundaries are
+    // multiples of 32, so every 32-column fragment lies in one group
+    int ngroups;
+    int gcol[kMaxGroups + 1];
+    const uint16_t *Qg[kMaxGroups];
     const uint16_t *C;  // nullable, leading dim ldy
     uint16_t *Y;
     int64_t ldy;
@@ -104,6 +112,27 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
 // LDS tile to row-major order, where C is added and y is rounded to BF16, so
 // that C is read and Y written in 16-byte chunks of 8 columns (8 lanes cover
 // 128 contiguous bytes of a row) instead of 2-byte accesses.
+// LoRA-up operands of the fragment at columns nb..nb+31: its T column offset
+// and the Q row of column n (clamped to the output).
+struct EpiLora {
+    const uint16_t *T;   // row mr of T at the group's first rank
+    const uint16_t *Q;   // Q row of the lane's column (its first rank)
+};
+
+__device__ __forceinline__ EpiLora epi_lora(const GemmArgs &p, int mb, int nb, int lane) {
+    const int lr = lane & 31;
+    const int mr = min(mb + lr, p.M - 1);
+    const int nr = min(nb + lr, p.N - 1);
+    int g = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i)
+        if (i < p.ngroups && nb >= p.gcol[i]) g = i;
+    EpiLora L;
+    L.T = p.T + (int64_t)mr * p.tld + g * p.rpad;
+    L.Q = p.ngroups > 1 ? p.Qg[g] + (int64_t)(nr - p.gcol[g]) * p.q_sn : p.Qs + (int64_t)nr * p.q_sn;
+    return L;
+}
+
 struct EpiIn {
     float dx[16];    // d_a of the lane's 16 rows
     float dw;        // d_b of the lane's column
@@ -131,15 +160,14 @@ __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int 
         }
     }
     if (epi_lora_prefetch(p)) {
-        const int mr = min(mb + lr, p.M - 1);
-        const int nr = min(n, p.N - 1);
+        const EpiLora L = epi_lora(p, mb, nb, lane);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int j0 = 16 * i + 8 * h;
             in.t[i] = u32x4{0u, 0u, 0u, 0u};
             in.q[i] = u32x4{0u, 0u, 0u, 0u};
-            if (16 * i < p.rpad) in.t[i] = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + j0);
-            if (j0 < p.r) in.q[i] = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
+            if (16 * i < p.rpad) in.t[i] = *reinterpret_cast<const u32x4 *>(L.T + j0);
+            if (j0 < p.r) in.q[i] = *reinterpret_cast<const u32x4 *>(L.Q + j0);
         }
     }
 }
@@ -161,22 +189,21 @@ __device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int 
                 a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, in.t[i]),
                                                             __builtin_bit_cast(bf16x8_t, in.q[i]), a, 0, 0, 0);
     } else if (p.T) {
-        const int mr = min(mb + lr, p.M - 1);
-        const int nr = min(n, p.N - 1);
+        const EpiLora L = epi_lora(p, mb, nb, lane);
         for (int kk = 0; kk < p.rpad; kk += 16) {
-            const u32x4 va = *reinterpret_cast<const u32x4 *>(p.T + (int64_t)mr * p.rpad + kk + 8 * h);
+            const u32x4 va = *reinterpret_cast<const u32x4 *>(L.T + kk + 8 * h);
             u32x4 vb;
             const int j0 = kk + 8 * h;
             if (p.q_sj == 1 && (p.r & 7) == 0) {
                 vb = u32x4{0u, 0u, 0u, 0u};
-                if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(p.Qs + (int64_t)nr * p.q_sn + j0);
+                if (j0 < p.r) vb = *reinterpret_cast<const u32x4 *>(L.Q + j0);
             } else {
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int ja = j0 + 2 * e, jb = ja + 1;
-                    const uint32_t lo = ja < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)ja * p.q_sj] : 0u;
-                    const uint32_t hi = jb < p.r ? p.Qs[(int64_t)nr * p.q_sn + (int64_t)jb * p.q_sj] : 0u;
+                    const uint32_t lo = ja < p.r ? L.Q[(int64_t)ja * p.q_sj] : 0u;
+                    const uint32_t hi = jb < p.r ? L.Q[(int64_t)jb * p.q_sj] : 0u;
                     w[e] = lo | (hi << 16);
                 }
                 vb = u32x4{w[0], w[1], w[2], w[3]};
@@ -302,6 +329,16 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
 }
 
 // ---- LoRA down-projection --------------------------------------------------
+// Row of P for rank j (ok: the rank exists; the pointer is valid either way).
+__device__ __forceinline__ const uint16_t *down_prow(const DownArgs &d, int j, bool &ok) {
+    if (d.ngroups > 1) {
+        const int g = min(j / d.grp_rpad, d.ngroups - 1), jj = j - g * d.grp_rpad;
+        ok = j < d.ngroups * d.grp_rpad && jj < d.r;
+        return d.Pg[g] + (int64_t)min(jj, d.r - 1) * d.p_sj;
+    }
+    ok = j < d.r;
+    return d.Ps + (int64_t)min(j, d.r - 1) * d.p_sj;
+}
 // T [M][rpad] = bf16(s . (Xl [M][Kl] . P^T)), P(j, k) = Ps[j p_sj + k p_sk] for
 // j < r, zero for r <= j < rpad; FP32 accumulation on v_mfma_f32_16x16x32_bf16.
 // The LoRA scale s is applied before the BF16 rounding; for a power-of-two s
@@ -351,16 +388,17 @@ __device__ __forceinline__ void lora_down_rows(const DownArgs &d, int m0, float 
                 va[u] = *reinterpret_cast<const u32x4 *>(xr + k);
 #pragma unroll
                 for (int f = 0; f < RG; ++f) {
-                    const int j = d.j0 + 16 * f + (lane & 15);
-                    if (j < d.r) {
+                    bool ok;
+                    const uint16_t *prow = down_prow(d, d.j0 + 16 * f + (lane & 15), ok);
+                    if (ok) {
                         if (d.p_sk == 1) {
-                            vb[u][f] = *reinterpret_cast<const u32x4 *>(d.Ps + (int64_t)j * d.p_sj + k);
+                            vb[u][f] = *reinterpret_cast<const u32x4 *>(prow + k);
                         } else {
                             uint32_t t[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                t[e] = (uint32_t)d.Ps[(int64_t)j * d.p_sj + (int64_t)(k + 2 * e) * d.p_sk] |
-                                       ((uint32_t)d.Ps[(int64_t)j * d.p_sj + (int64_t)(k + 2 * e + 1) * d.p_sk] << 16);
+                                t[e] = (uint32_t)prow[(int64_t)(k + 2 * e) * d.p_sk] |
+                                       ((uint32_t)prow[(int64_t)(k + 2 * e + 1) * d.p_sk] << 16);
                             vb[u][f] = u32x4{t[0], t[1], t[2], t[3]};
                         }
                     }
@@ -456,11 +494,7 @@ __global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArg
     const uint16_t *pr[RG];
     bool jok[RG];
 #pragma unroll
-    for (int f = 0; f < RG; ++f) {
-        const int j = d.j0 + 16 * f + li;
-        jok[f] = j < d.r;
-        pr[f] = d.Ps + (int64_t)min(j, d.r - 1) * d.p_sj;
-    }
+    for (int f = 0; f < RG; ++f) pr[f] = down_prow(d, d.j0 + 16 * f + li, jok[f]);
     float xdm[RPW];
     if (NV) {
 #pragma unroll
@@ -577,24 +611,29 @@ __global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArg
     }
 }
 
+// Ranks in passes of up to 64 (each pass reads X again); the side work rides
+// on the first pass.
 template <bool NV>
 static pact_status launch_down_pipe(DownArgs d, hipStream_t st) {
-    const int rg = d.rpad / 16;
-    const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
-    const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) + (NV ? d.side_wgs : 0))),
-        block(64 * kPipeWaves);
-    d.j0 = 0;
+    for (int j0 = 0; j0 < d.rpad; j0 += 64) {
+        const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
+        const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
+        const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) + (NV && j0 == 0 ? d.side_wgs : 0))),
+            block(64 * kPipeWaves);
+        d.j0 = j0;
 #define PACT_DOWN_PIPE(RG)                                                                        \
     if (two) hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 2, NV>), grid, block, 0, st, d);      \
     else hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 1, NV>), grid, block, 0, st, d);
-    switch (rg) {
-        case 1: PACT_DOWN_PIPE(1) break;
-        case 2: PACT_DOWN_PIPE(2) break;
-        case 3: PACT_DOWN_PIPE(3) break;
-        default: PACT_DOWN_PIPE(4) break;
-    }
+        switch (rg) {
+            case 1: PACT_DOWN_PIPE(1) break;
+            case 2: PACT_DOWN_PIPE(2) break;
+            case 3: PACT_DOWN_PIPE(3) break;
+            default: PACT_DOWN_PIPE(4) break;
+        }
 #undef PACT_DOWN_PIPE
-    return launch_status();
+        PACT_TRY(launch_status());
+    }
+    return PACT_OK;
 }
 
 pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st) {
@@ -603,7 +642,7 @@ pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st) {
 }
 
 pact_status launch_lora_down(DownArgs d, hipStream_t st) {
-    if (d.rpad <= 64 && d.p_sk == 1) return launch_down_pipe<false>(d, st);
+    if (d.p_sk == 1) return launch_down_pipe<false>(d, st);
     const dim3 grid((unsigned)((d.M + 15) / 16)), block(64 * kDownWaves);
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         d.j0 = j0;
@@ -1410,14 +1449,24 @@ static pact_status launch_plan(const GemmArgs &a, int kernel, hipStream_t st) {
     return PACT_OK;
 }
 
+// Projections of a grouped forward GEMM: output columns [col[g], col[g + 1])
+// with LoRA A = P[g] [r][K], B = Q[g] [col[g + 1] - col[g]][r].
+struct LoraGroups {
+    int n;
+    int col[kMaxGroups + 1];
+    const uint16_t *P[kMaxGroups];
+    const uint16_t *Q[kMaxGroups];
+};
+
 // Shared body of the forward and input-gradient entry points.
 //   aq [M][Kc] NVFP4, bq [Nout][Kc] NVFP4, Xl [M][Kl] BF16 LoRA input,
-//   P(j, k) = Psrc[j p_sj + k p_sk] (j < r, k < Kl), Q(n, j) = Qsrc[n q_sn + j q_sj].
+//   P(j, k) = Psrc[j p_sj + k p_sk] (j < r, k < Kl), Q(n, j) = Qsrc[n q_sn + j q_sj];
+//   or, with groups, the block-diagonal LoRA of groups->n projections (rank r each).
 static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const uint16_t *Xl,
                                int64_t ldx, int64_t Kl, const pact_lora *lora, const uint16_t *Psrc,
                                int64_t p_sj, int64_t p_sk, const uint16_t *Qsrc, int64_t q_sn,
                                int64_t q_sj, const uint16_t *C, uint16_t *Y, int64_t ldy, void *ws,
-                               size_t ws_bytes, void *stream) {
+                               size_t ws_bytes, void *stream, const LoraGroups *groups = nullptr) {
     if (!aq || !bq) return PACT_ERR_INVALID_ARG;
     const int64_t M = aq->rows, Kc = aq->cols, Nout = bq->rows;
     if (M < 0 || Kc < 0 || Nout < 0 || bq->cols != Kc) return PACT_ERR_INVALID_ARG;
@@ -1454,7 +1503,8 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     a.C = C;
     a.Y = Y;
     a.ldy = ldy;
-    const size_t t_bytes = lora_ws_bytes(M, r);
+    const int ng = groups && r > 0 ? groups->n : 1;
+    const size_t t_bytes = lora_ws_bytes(M, ng * (int)round_up(r, 16));
     if (r > 0) {
         if (!ws || ws_bytes < t_bytes) return PACT_ERR_WORKSPACE;
         if (!aligned16(ws)) return PACT_ERR_MISALIGNED;
@@ -1469,8 +1519,18 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     if (r > 0) {
         const int rpad = (int)round_up(r, 16);
         uint16_t *T = static_cast<uint16_t *>(ws);
-        DownArgs d = {Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, rpad, 0, lora->scale, T};
-        if (plan.ks > 1 && rpad <= 64)
+        DownArgs d = {Xl, ldx, (int)M, (int)Kl, Psrc, p_sj, p_sk, r, ng * rpad, 0, lora->scale, T};
+        a.ngroups = ng;
+        if (ng > 1) {
+            d.ngroups = ng;
+            d.grp_rpad = rpad;
+            for (int g = 0; g < ng; ++g) {
+                d.Pg[g] = groups->P[g];
+                a.Qg[g] = groups->Q[g];
+            }
+            for (int g = 0; g <= ng; ++g) a.gcol[g] = groups->col[g];
+        }
+        if (plan.ks > 1 && ng * rpad <= 64)
             a.down = d;  // computed by workgroups of the split-K main kernel
         else
             PACT_TRY(launch_lora_down(d, st));
@@ -1480,6 +1540,7 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
         a.q_sj = q_sj;
         a.r = r;
         a.rpad = rpad;
+        a.tld = ng * rpad;
     }
     return launch_plan(a, plan.kernel, st);
 }
@@ -1512,6 +1573,45 @@ extern "C" pact_status pact_gemm_nvfp4_fwd(const pact_nvfp4 *Xq, const uint16_t 
     return gemm_common(Xq, W_fwd, X, ld_x, K, lora, lora ? lora->A : nullptr, K, 1,
                        lora ? lora->B : nullptr, r, 1, C, Y, ld_y, ws, ws_bytes, stream);
     (void)N;
+}
+
+extern "C" pact_status pact_gemm_nvfp4_fwd_grouped(const pact_nvfp4 *Xq, const uint16_t *X, int64_t ld_x,
+                                                   const pact_nvfp4 *W_fwd, int32_t ngroups,
+                                                   const int64_t *group_rows, const pact_lora *loras,
+                                                   uint16_t *Y, int64_t ld_y, void *ws, size_t ws_bytes,
+                                                   void *stream) {
+    if (!Xq || !W_fwd || !group_rows || ngroups < 1 || ngroups > kMaxGroups) return PACT_ERR_INVALID_ARG;
+    const int64_t K = Xq->cols;
+    LoraGroups gr = {};
+    gr.n = ngroups;
+    int64_t col = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        if (group_rows[g] < 0) return PACT_ERR_INVALID_ARG;
+        if (group_rows[g] % 32 != 0) return PACT_ERR_UNSUPPORTED_SHAPE;
+        gr.col[g] = (int)col;
+        col += group_rows[g];
+        if (col > INT32_MAX) return PACT_ERR_UNSUPPORTED_SHAPE;
+    }
+    gr.col[ngroups] = (int)col;
+    if (col != W_fwd->rows) return PACT_ERR_INVALID_ARG;
+    int r = 0;
+    float scale = 0.0f;
+    if (loras) {
+        r = loras[0].r;
+        scale = loras[0].scale;
+        for (int g = 0; g < ngroups; ++g) {
+            if (loras[g].r != r || loras[g].scale != scale) return PACT_ERR_INVALID_ARG;
+            if (r > 0 && (!loras[g].A || !loras[g].B)) return PACT_ERR_INVALID_ARG;
+            if (r > 0 && (!aligned16(loras[g].A) || !aligned16(loras[g].B))) return PACT_ERR_MISALIGNED;
+            gr.P[g] = loras[g].A;
+            gr.Q[g] = loras[g].B;
+        }
+        if (r < 0 || ngroups * round_up(r, 16) > 256) return PACT_ERR_INVALID_ARG;
+    }
+    const pact_lora lo = {gr.P[0], gr.Q[0], r, scale};
+    // T = X [A_0; A_1; ...]^T (ranks of group g at g round_up(r, 16)), block-diagonal LoRA-up
+    return gemm_common(Xq, W_fwd, X, ld_x, K, r > 0 ? &lo : nullptr, gr.P[0], K, 1, gr.Q[0], r, 1, nullptr, Y,
+                       ld_y, ws, ws_bytes, stream, r > 0 ? &gr : nullptr);
 }
 
 extern "C" pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16_t *dY,

@@ -44,6 +44,8 @@ inline pact_status launch_status() {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+constexpr int kMaxGroups = 4;  // projections of one grouped GEMM
+
 // LoRA-down product T [M][rpad] = bf16(s . (X [M][Kl] . P^T)) over ranks
 // j0 .. j0 + 64 (P(j, k) = Ps[j p_sj + k p_sk], zero for j >= r); launched by
 // launch_lora_down (all ranks) and fused into split-K GEMM launches.  X is
@@ -60,6 +62,10 @@ struct DownArgs {
     uint16_t *T;
     const uint8_t *xc, *xs;  // NVFP4 source: codes [M][Kl/2], scales [M][Kl/16]
     const float *xd;         // and row scales [M]
+    // grouped LoRA (ngroups > 1, p_sk == 1): ranks come in ngroups blocks of
+    // grp_rpad, rank j of block g = j / grp_rpad is row j % grp_rpad (< r) of Pg[g]
+    int ngroups, grp_rpad;
+    const uint16_t *Pg[4];
     // extra workgroups of launch_lora_down_nvfp4 (side_wgs of them) write
     // Bt [side_r][side_N] = B^T (B [side_N][side_r])
     int side_wgs;

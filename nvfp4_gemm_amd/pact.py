@@ -40,7 +40,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
-           "pact_lora_grads_nvfp4", "pact_adamw_step"]
+           "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped"]
 
 
 class PactError(RuntimeError):
@@ -89,6 +89,9 @@ def lib():
         L.pact_lora_grads_workspace.argtypes = [I64, I64, I64, ctypes.c_int32]
         L.pact_lora_grads_nvfp4.restype = st
         L.pact_lora_grads_nvfp4.argtypes = [NV, P, I64, I64, LO, P, P, P, ctypes.c_size_t, P]
+        L.pact_gemm_nvfp4_fwd_grouped.restype = st
+        L.pact_gemm_nvfp4_fwd_grouped.argtypes = [NV, P, I64, NV, ctypes.c_int32, ctypes.POINTER(I64),
+                                                  LO, P, I64, P, ctypes.c_size_t, P]
         L.pact_adamw_step.restype = st
         L.pact_adamw_step.argtypes = [P, P, P, P, P, I64, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, I64, P]
         L.pact_debug_dsilu32.restype = st
@@ -148,6 +151,13 @@ class NVFP4Tensor:
 
     def nbytes(self):
         return self.codes.numel() + self.scales.numel() + 4 * self.row_scale.numel()
+
+    @staticmethod
+    def cat_rows(parts):
+        """Row-wise concatenation (one copy), e.g. the forward layouts of the
+        projections of a grouped GEMM."""
+        return NVFP4Tensor(torch.cat([q.codes for q in parts]), torch.cat([q.scales for q in parts]),
+                           torch.cat([q.row_scale for q in parts]))
 
 
 def _desc_ref(q):
@@ -273,6 +283,29 @@ def pact_gemm_nvfp4_fwd(Xq: NVFP4Tensor, W_fwd: NVFP4Tensor, X=None, lora: LoRA 
     """Y = bf16(d_x d_w Xq.W_fwd^T + s bf16(X A^T) B^T (+ C))."""
     return _gemm(lib().pact_gemm_nvfp4_fwd, "pact_gemm_nvfp4_fwd", Xq, X, W_fwd, lora, C, Y, ws,
                  stream)
+
+
+def pact_gemm_nvfp4_fwd_grouped(Xq: NVFP4Tensor, W_cat: NVFP4Tensor, group_rows, X=None, loras=None, Y=None,
+                                ws=None, stream=None):
+    """The projections of W_cat (rows group_rows[0], group_rows[1], ...) as one
+    GEMM with a block-diagonal LoRA term: Y [M][sum group_rows]."""
+    M, Nout = Xq.rows, W_cat.rows
+    ng = len(group_rows)
+    if Y is None:
+        Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=Xq.codes.device)
+    r = loras[0].r if loras else 0
+    if ws is None:
+        need = pact_gemm_workspace(M, Nout, Xq.cols, ng * ((r + 15) // 16 * 16) if r else 0)
+        if need > 0:
+            ws = torch.empty((need,), dtype=torch.uint8, device=Xq.codes.device)
+    rows = (ctypes.c_int64 * ng)(*[int(n) for n in group_rows])
+    lo = (pact_lora * ng)(*[l.desc() for l in loras]) if loras else None
+    dx, dw = Xq.desc(), W_cat.desc()
+    _check(lib().pact_gemm_nvfp4_fwd_grouped(ctypes.byref(dx), _ptr(X), _ld(X) if X is not None else 0,
+                                             ctypes.byref(dw), ng, rows, lo, _ptr(Y), _ld(Y), _ptr(ws),
+                                             ws.numel() if ws is not None else 0, _stream(stream)),
+           "pact_gemm_nvfp4_fwd_grouped")
+    return Y
 
 
 def pact_gemm_nvfp4_dgrad(dYq: NVFP4Tensor, W_bwd: NVFP4Tensor, dY=None, lora: LoRA | None = None,
