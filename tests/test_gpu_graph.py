@@ -56,3 +56,83 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for i, (t, r0) in enumerate(zip(outs, ref)):
             assert torch.equal(t.view(torch.uint8), r0.view(torch.uint8)), f"replay {rep}: output {i} differs"
+
+
+def test_graph_replay_grouped_grads_adamw():
+    """Grouped forward, LoRA weight gradients (side workgroups, split partials)
+    and the AdamW step captured in one graph: every replay, with eager work in
+    between, equals the eager run.  AdamW updates its state in place, so the
+    state is reset to the same values before each replay and before the eager
+    reference."""
+    from nvfp4_gemm_amd import pact as pb
+    from tests import _gpu as G
+
+    M, H, KV, r = 512, 512, 128, 16
+    rng = np.random.default_rng(8)
+    X = G.dev_bf16(synth.student_t_bf16(rng, (M, H), 4.0, 0.5))
+    Xq = pb.pact_quantize_nvfp4(X)
+    rows = [H, KV, KV]
+    Wf = pb.NVFP4Tensor.cat_rows([pb.pact_build_weight_layouts(G.dev_bf16(synth.weight_bf16(rng, n, H)))[0]
+                                  for n in rows])
+    n_par = sum(r * H + n * r for n in rows)
+    wflat = torch.empty(n_par, dtype=torch.bfloat16, device="cuda")
+    gflat = torch.zeros(n_par, dtype=torch.float32, device="cuda")
+    loras, gviews, off = [], [], 0
+    for n in rows:
+        A = wflat[off:off + r * H].view(r, H)
+        A.copy_(G.dev_bf16(synth.normal_bf16(rng, (r, H), 0.02)))
+        gA = gflat[off:off + r * H].view(r, H)
+        off += r * H
+        B = wflat[off:off + n * r].view(n, r)
+        B.copy_(G.dev_bf16(synth.normal_bf16(rng, (n, r), 0.01)))
+        gB = gflat[off:off + n * r].view(n, r)
+        off += n * r
+        loras.append(pb.LoRA(A, B, 2.0))
+        gviews.append((gA, gB))
+    p0 = wflat.float()
+    p, m, v = p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)
+    w_out = torch.empty_like(wflat)
+    Y = torch.empty((M, H + 2 * KV), dtype=torch.bfloat16, device="cuda")
+    dY = G.dev_bf16(synth.normal_bf16(rng, (M, H + 2 * KV), 1.0))
+    ws = torch.empty((pb.pact_gemm_workspace(M, H + 2 * KV, H, 3 * r),), dtype=torch.uint8, device="cuda")
+    gws = torch.empty((max(pb.pact_lora_grads_workspace(M, n, H, r) for n in rows),), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        pb.pact_gemm_nvfp4_fwd_grouped(Xq, Wf, rows, X=X, loras=loras, Y=Y, ws=ws)
+        c = 0
+        for g, n in enumerate(rows):
+            pb.pact_lora_grads_nvfp4(Xq, dY[:, c:c + n], loras[g], dA=gviews[g][0], dB=gviews[g][1], ws=gws)
+            c += n
+        pb.pact_adamw_step(p, m, v, gflat, w_out, lr=1e-3, weight_decay=0.01, step=3)
+
+    def reset():
+        p.copy_(p0)
+        m.zero_()
+        v.zero_()
+
+    outs = [Y, gflat, p, m, v, w_out]
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (Y, gflat, w_out):
+            t.zero_()
+        reset()
+        pb.pact_quantize_nvfp4(X, pb.NVFP4Tensor.empty(M, H))     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, r0) in enumerate(zip(outs, ref)):
+            assert torch.equal(t.view(torch.uint8), r0.view(torch.uint8)), f"replay {rep}: output {i} differs"
