@@ -1401,14 +1401,26 @@ static size_t lora_ws_bytes(int64_t M, int32_t r) {
     return (size_t)round_up(M * round_up(r, 16) * 2, 256);
 }
 
-// Workspace of one projection: the LoRA-down product and the split-K
-// partials of either direction (forward [M][N] over K, input gradient
-// [M][K] over N).
+// B^T [r][N] for the input gradient's LoRA-down (so its rank operand has
+// contiguous rows).
+static size_t bt_bytes(int64_t N, int32_t r) { return r > 0 ? (size_t)round_up((int64_t)r * N * 2, 256) : 0; }
+
+// Workspace of one projection: the LoRA-down product, the split-K partials of
+// either direction (forward [M][N] over K, input gradient [M][K] over N) and
+// B^T.
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     const int cus = device_cus();
     const GemmPlan f = plan_gemm(M, N, K, cus), b = plan_gemm(M, K, N, cus);
     const size_t pf = partial_bytes(M, N, f.ks), pb = partial_bytes(M, K, b.ks);
-    return lora_ws_bytes(M, r) + (pf > pb ? pf : pb);
+    return lora_ws_bytes(M, r) + (pf > pb ? pf : pb) + bt_bytes(N, r);
+}
+
+// Pt [r][Kl] = P^T for P [Kl][r] row-major (the input gradient's B).
+__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t *P, int Kl, int r, uint16_t *Pt) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)Kl * r) return;
+    const int j = (int)(i / Kl), k = (int)(i % Kl);
+    Pt[i] = P[(int64_t)k * r + j];
 }
 
 template <int WM, int WN, int WK>
@@ -1530,10 +1542,24 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
             }
             for (int g = 0; g <= ng; ++g) a.gcol[g] = groups->col[g];
         }
-        if (plan.ks > 1 && ng * rpad <= 64)
+        const size_t bt_off = t_bytes + (plan.ks > 1 ? p_bytes : 0);
+        if (plan.ks > 1 && ng * rpad <= 64) {
             a.down = d;  // computed by workgroups of the split-K main kernel
-        else
+        } else if (d.p_sk == (int64_t)r && d.p_sj == 1 && M >= 4096 &&
+                   ws_bytes >= bt_off + bt_bytes(Kl, r)) {
+            // rank operand with strided rows (the input gradient's B [N][r]):
+            // transpose it once so the pipelined LoRA-down reads contiguous rows
+            uint16_t *Pt = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + bt_off);
+            hipLaunchKernelGGL(lora_transpose_kernel, dim3((unsigned)((Kl * r + 255) / 256)), dim3(256), 0, st, Psrc,
+                               (int)Kl, r, Pt);
+            PACT_TRY(launch_status());
+            d.Ps = Pt;
+            d.p_sj = Kl;
+            d.p_sk = 1;
             PACT_TRY(launch_lora_down(d, st));
+        } else {
+            PACT_TRY(launch_lora_down(d, st));
+        }
         a.T = T;
         a.Qs = Qsrc;
         a.q_sn = q_sn;
