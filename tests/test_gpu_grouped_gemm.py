@@ -88,3 +88,27 @@ def test_grouped_validation():
         pb.pact_gemm_nvfp4_fwd_grouped(xq, W, [64, 16, 16])   # groups must be multiples of 32
     with pytest.raises(RuntimeError):
         pb.pact_gemm_nvfp4_fwd_grouped(xq, W, [64, 64])       # rows do not add up
+
+
+def test_grouped_fwd_strided_x_and_y():
+    """X read through a leading dimension > K and Y written into a column range
+    of a wider buffer; columns outside it are left untouched."""
+    M, K, rows, r = 96, 256, [128, 64], 16
+    rng = np.random.default_rng(4)
+    Xh = synth.student_t_bf16(rng, (M, K), 4.0, 0.5)
+    xq = oracle.quantize_bf16(Xh)
+    Ws = [synth.weight_bf16(rng, n, K) for n in rows]
+    As = [synth.normal_bf16(rng, (r, K), 0.02) for _ in rows]
+    Bs = [synth.normal_bf16(rng, (n, r), 0.01) for n in rows]
+    refs = [oracle.gemm_fwd(xq, Xh, oracle.build_weight_layouts(W)[0], A, B, 2.0) for W, A, B in zip(Ws, As, Bs)]
+    Xw = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    Xw[:, 64:] = G.dev_bf16(Xh)
+    gW = pb.NVFP4Tensor.cat_rows([pb.pact_build_weight_layouts(G.dev_bf16(W))[0] for W in Ws])
+    loras = [pb.LoRA(G.dev_bf16(A), G.dev_bf16(B), 2.0) for A, B in zip(As, Bs)]
+    Yw = torch.full((M, sum(rows) + 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    pb.pact_gemm_nvfp4_fwd_grouped(G.dev_nvfp4(xq), gW, rows, X=Xw[:, 64:], loras=loras, Y=Yw[:, 32:32 + sum(rows)])
+    torch.cuda.synchronize()
+    Yh = G.host_bits(Yw)
+    G.check_gemm_tolerance(np.ascontiguousarray(Yh[:, 32:32 + rows[0]]), refs[0], "group 0 strided")
+    G.check_gemm_tolerance(np.ascontiguousarray(Yh[:, 32 + rows[0]:32 + sum(rows)]), refs[1], "group 1 strided")
+    assert torch.all(Yw[:, :32] == 7.0) and torch.all(Yw[:, 32 + sum(rows):] == 7.0)

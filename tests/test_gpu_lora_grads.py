@@ -86,3 +86,18 @@ def test_lora_grads_no_tokens():
     torch.cuda.synchronize()
     assert torch.all(dA == 0) and torch.all(dB == 0)
     del xq
+
+
+def test_lora_grads_strided_dy():
+    """dY as a column slice of a wider buffer (leading dimension > N), as the
+    layer bench passes the k and v gradients."""
+    M, N, K, r = 300, 128, 256, 16
+    xq, dY, A, B = _case(M, N, K, r, seed=77)
+    dA, dB = oracle.lora_grads(xq, dY, A, B, 2.0)
+    wide = torch.zeros((M, N + 96), dtype=torch.bfloat16, device="cuda")
+    wide[:, 32:32 + N] = G.dev_bf16(dY)
+    lora = pb.LoRA(G.dev_bf16(A), G.dev_bf16(B), 2.0)
+    gdA, gdB = pb.pact_lora_grads_nvfp4(G.dev_nvfp4(xq), wide[:, 32:32 + N], lora)
+    torch.cuda.synchronize()
+    _check(gdA, dA, "dA strided dY")
+    _check(gdB, dB, "dB strided dY")
