@@ -229,14 +229,16 @@ struct GradPlan {
     int cb, msplit, mchunk;
 };
 
-// CB = 256 columns for wide outputs (the rank operand is re-read once per
-// column block), 128 otherwise; token splits for about 512 workgroups, with at
-// least 4 stages per workgroup and at most kMaxSplits.
-static GradPlan grad_plan(int64_t M, int64_t C) {
-    const int cb = C >= 4096 ? 256 : 128;
+// CB = 256 columns for wide BF16 outputs with many tokens (the rank operand
+// is re-read once per column block), 128 otherwise; token splits for about 512
+// workgroups, down to one stage per workgroup and at most kMaxSplits (swept
+// on the box over the layer shapes: at M = 1024 the extra splits take a
+// contraction from 13-19 to 9-15 us).
+static GradPlan grad_plan(int64_t M, int64_t C, bool nv) {
+    const int cb = (!nv && C >= 4096 && M >= 4096) ? 256 : 128;
     const int64_t cblocks = (C + cb - 1) / cb;
     int64_t ms = (512 + cblocks - 1) / cblocks;
-    int64_t max_ms = (M + 4 * kGradMT - 1) / (4 * kGradMT);
+    int64_t max_ms = (M + kGradMT - 1) / kGradMT;
     if (max_ms > kMaxSplits) max_ms = kMaxSplits;
     if (ms > max_ms) ms = max_ms;
     if (ms < 1) ms = 1;
@@ -246,8 +248,8 @@ static GradPlan grad_plan(int64_t M, int64_t C) {
     return {cb, (int)(ms > 0 ? ms : 1), (int)mchunk};
 }
 
-static size_t grad_part_bytes(int64_t M, int64_t C, int r) {
-    const GradPlan p = grad_plan(M, C);
+static size_t grad_part_bytes(int64_t M, int64_t C, int r, bool nv) {
+    const GradPlan p = grad_plan(M, C, nv);
     const int jt = (r + 31) / 32;
     return (size_t)round_up((int64_t)p.msplit * C * 32 * jt * 4, 256);
 }
@@ -258,7 +260,7 @@ static size_t lora_grads_ws(int64_t M, int64_t N, int64_t K, int r) {
     const int64_t rpad = round_up(r, 16);
     const size_t t = (size_t)round_up(M * rpad * 2, 256);
     const size_t bt = (size_t)round_up((int64_t)r * N * 2, 256);
-    return 2 * t + bt + grad_part_bytes(M, N, r) + grad_part_bytes(M, K, r);
+    return 2 * t + bt + grad_part_bytes(M, N, r, false) + grad_part_bytes(M, K, r, true);
 }
 
 template <bool NV>
@@ -277,7 +279,7 @@ static void launch_grad_kernel(const GradArgs &g, const GradPlan &p, int jt, hip
 // plus g.side's reduction in extra workgroups; returns the reduction of this
 // contraction's partials into out[c * osc + j * osj].
 static RedArgs launch_grad(GradArgs g, float *out, int64_t osc, int64_t osj, hipStream_t st, pact_status *status) {
-    const GradPlan p = grad_plan(g.M, g.C);
+    const GradPlan p = grad_plan(g.M, g.C, g.vc != nullptr);
     const int jt = (g.r + 31) / 32;
     g.mchunk = p.mchunk;
     g.cblocks = (g.C + p.cb - 1) / p.cb;
@@ -330,7 +332,7 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     uint16_t *Bt = reinterpret_cast<uint16_t *>(base);
     base += round_up((int64_t)r * N * 2, 256);
     float *partB = reinterpret_cast<float *>(base);
-    float *partA = reinterpret_cast<float *>(base + grad_part_bytes(M, N, r));
+    float *partA = reinterpret_cast<float *>(base + grad_part_bytes(M, N, r, false));
     // T^ = bf16(s X^ A^T) straight from the NVFP4 rows (P(j, k) = A[j K + k]);
     // its side workgroups write B^T
     DownArgs dh{};
