@@ -61,12 +61,16 @@ struct GemmArgs {
     const uint16_t *C;  // nullable, leading dim ldy
     uint16_t *Y;
     int64_t ldy;
+    uint32_t y_rec;  // M * ldy * 2 when below 2^31 (Y and C then go through buffer descriptors), else 0
     int ks;       // K ranges split across workgroups (blockIdx.y); 1: no split
     float *part;  // ks > 1: FP32 partial fragments [ks][ceil(M/32)][ceil(N/32)][1024]
     DownArgs down;  // ks > 1 and down.X: the LoRA-down runs as workgroups blockIdx.y == 0
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Word 3 of the buffer resource descriptors (raw buffer access).
+constexpr int kRsrcWord3 = 0x00020000;
 
 // 16-byte direct global->LDS load: lane l of the wavefront writes 16 bytes at
 // lds_base + 16 l (lds_base is wavefront-uniform).
@@ -242,7 +246,47 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const floa
     const int rr = lane / LPR, c = 8 * (lane % LPR);
     const int n = nb0 + c;
     const bool full = n + 8 <= p.N;
+    // y = bf16(tile + C) for the 8 columns of row `row` (tile row), C words cw
+    auto finish8 = [&](int row, const u32x4 &cq, uint32_t o[4]) {
+        const float4_t v0 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c);
+        const float4_t v1 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c + 4);
+        float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if (p.C) {
+            const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = y[j] + ((j & 1) ? bf16_hi(cw[j >> 1]) : bf16_lo(cw[j >> 1]));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_bits(y[2 * j]) | (f32_to_bf16_bits(y[2 * j + 1]) << 16);
+    };
     u32x4 cv[NQ];
+    if (full && p.y_rec) {
+        // 32-bit offsets into buffer descriptors of Y and C: rows at or past M
+        // lie beyond the descriptor's records, so their loads read zero and
+        // their stores are dropped, with no per-row address arithmetic or test
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void *)p.Y, (short)0, (int)p.y_rec,
+                                                                           kRsrcWord3);
+        const uint32_t off0 = ((uint32_t)(mb + rr) * (uint32_t)p.ldy + (uint32_t)n) * 2u;
+        const uint32_t step = (uint32_t)RPI * (uint32_t)p.ldy * 2u;
+        if (p.C) {
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void *)p.C, (short)0,
+                                                                               (int)p.y_rec, kRsrcWord3);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(off0 + (uint32_t)q * step), 0, 0);
+                cv[q] = u32x4{v[0], v[1], v[2], v[3]};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            uint32_t o[4];
+            finish8(RPI * q + rr, p.C ? cv[q] : u32x4{0u, 0u, 0u, 0u}, o);
+            typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+            __builtin_amdgcn_raw_buffer_store_b128(u4_t{o[0], o[1], o[2], o[3]}, ry, (int)(off0 + (uint32_t)q * step),
+                                                   0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int m = mb + RPI * q + rr;
@@ -265,17 +309,8 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const floa
         const int row = RPI * q + rr;
         const int m = mb + row;
         if (m >= p.M) continue;
-        const float4_t v0 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c);
-        const float4_t v1 = *reinterpret_cast<const float4_t *>(tile + row * epi_tile_stride<G>() + c + 4);
-        float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        if (p.C) {
-            const uint32_t cw[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = y[j] + ((j & 1) ? bf16_hi(cw[j >> 1]) : bf16_lo(cw[j >> 1]));
-        }
         uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_bits(y[2 * j]) | (f32_to_bf16_bits(y[2 * j + 1]) << 16);
+        finish8(row, cv[q], o);
         uint16_t *dst = p.Y + (int64_t)m * p.ldy + n;
         if (full) {
             *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
@@ -721,7 +756,7 @@ __device__ __forceinline__ void finish_frags(const GemmArgs &p, int lane, AccFn 
 // barrier per stage; a single-wavefront group needs none.
 constexpr int kNBuf = 4;   // LDS stage buffers per group
 // Buffer descriptor word 3 for raw (untyped, unswizzled) byte access on gfx950.
-constexpr int kRsrcWord3 = 0x00020000;
+
 constexpr int kSK = 64;    // K per stage
 
 template <int N>
@@ -1515,6 +1550,7 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     a.C = C;
     a.Y = Y;
     a.ldy = ldy;
+    a.y_rec = M * ldy * 2 < ((int64_t)1 << 31) ? (uint32_t)(M * ldy * 2) : 0u;
     const int ng = groups && r > 0 ? groups->n : 1;
     const size_t t_bytes = lora_ws_bytes(M, ng * (int)round_up(r, 16));
     if (r > 0) {
