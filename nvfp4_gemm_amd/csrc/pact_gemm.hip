@@ -147,6 +147,8 @@ __device__ __forceinline__ bool epi_lora_prefetch(const GemmArgs &p) {
     return p.T && p.rpad <= 32 && p.q_sj == 1 && (p.r & 7) == 0;
 }
 
+// The prefetched LoRA operands are read through buffer descriptors (base in
+// scalar registers, 32-bit offsets, in range by construction: clamped rows).
 __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int lane, EpiIn &in) {
     const int h = lane >> 5, lr = lane & 31;
     const int n = nb + lr;
@@ -164,14 +166,31 @@ __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int 
         }
     }
     if (epi_lora_prefetch(p)) {
-        const EpiLora L = epi_lora(p, mb, nb, lane);
+        const int mr = min(mb + lr, p.M - 1);
+        const int nr = min(n, p.N - 1);
+        int g = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxGroups; ++i)
+            if (i < p.ngroups && nb >= p.gcol[i]) g = i;
+        const uint16_t *qb = p.ngroups > 1 ? p.Qg[g] : p.Qs;
+        const int qrow = p.ngroups > 1 ? nr - p.gcol[g] : nr;
+        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc((void *)p.T, (short)0, 0x7FFFFFFF, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, (short)0, 0x7FFFFFFF, kRsrcWord3);
+        const int toff = 2 * (mr * p.tld + g * p.rpad);
+        const int qoff = 2 * (qrow * (int)p.q_sn);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int j0 = 16 * i + 8 * h;
             in.t[i] = u32x4{0u, 0u, 0u, 0u};
             in.q[i] = u32x4{0u, 0u, 0u, 0u};
-            if (16 * i < p.rpad) in.t[i] = *reinterpret_cast<const u32x4 *>(L.T + j0);
-            if (j0 < p.r) in.q[i] = *reinterpret_cast<const u32x4 *>(L.Q + j0);
+            if (16 * i < p.rpad) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rt, toff + 2 * j0, 0, 0);
+                in.t[i] = u32x4{v[0], v[1], v[2], v[3]};
+            }
+            if (j0 < p.r) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 2 * j0, 0, 0);
+                in.q[i] = u32x4{v[0], v[1], v[2], v[3]};
+            }
         }
     }
 }
