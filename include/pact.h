@@ -154,7 +154,8 @@ pact_status pact_build_weight_layouts(const uint16_t *W, const pact_nvfp4 *W_fwd
  * over K; input gradient: [M][K] over N) with LoRA rank r: the LoRA-down
  * product [M][r rounded up to 16] BF16, then room for FP32 partial sums when
  * the launch plan splits K across workgroups (small outputs with long K), then
- * B^T [r][N] (the input gradient's LoRA-down reads it when M >= 4096).
+ * B^T [r][N] (the input gradient's LoRA-down reads it when M >= 4096) and
+ * A^T [K][r] (the input gradient's LoRA-up reads it when r % 8 == 0).
  * A GEMM given less than this but at least the LoRA-down product runs
  * without the K split; results are within the same tolerance either way and
  * bit-identical across runs with the same workspace size. */

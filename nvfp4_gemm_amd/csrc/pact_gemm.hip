@@ -482,8 +482,19 @@ __device__ __forceinline__ void lora_down_rows(const DownArgs &d, int m0, float 
     __syncthreads();  // red is reused by the caller's next row group
 }
 
+// The side job of d as workgroup wg of nwg (no barriers: side workgroups
+// return before the launch's own work).
+__device__ __forceinline__ void side_transpose(const DownArgs &d, int64_t wg, int64_t nwg) {
+    const int64_t nt = (int64_t)d.side_N * d.side_r;
+    for (int64_t i = wg * blockDim.x + threadIdx.x; i < nt; i += nwg * blockDim.x) {
+        const int j = (int)(i / d.side_N), n = (int)(i % d.side_N);
+        d.side_Bt[i] = d.side_B[(int64_t)n * d.side_r + j];
+    }
+}
+
 // LoRA-down as workgroups of a split-K main kernel (which does not read T):
-// row groups blockIdx.x, blockIdx.x + gridDim.x, ...; ranks up to 64.
+// row groups blockIdx.x, blockIdx.x + gridDim.x, ...; ranks up to 64.  The
+// side job follows, spread over the same workgroups.
 template <int NW>
 __device__ __forceinline__ void lora_down_fused(const DownArgs &d, float *red) {
     const int groups = (d.M + 15) / 16;
@@ -495,6 +506,7 @@ __device__ __forceinline__ void lora_down_fused(const DownArgs &d, float *red) {
             default: lora_down_rows<4, NW>(d, 16 * g, red); break;
         }
     }
+    if (d.side_Bt) side_transpose(d, blockIdx.x, gridDim.x);
 }
 
 constexpr int kDownWaves = 16;
@@ -502,6 +514,11 @@ constexpr int kDownWaves = 16;
 template <int RG>
 __global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
     __shared__ float red[down_red_floats<RG, kDownWaves>()];
+    const int groups = (d.M + 15) / 16;
+    if ((int)blockIdx.x >= groups) {  // side job (whole workgroups, before any barrier)
+        side_transpose(d, blockIdx.x - groups, gridDim.x - groups);
+        return;
+    }
     lora_down_rows<RG, kDownWaves>(d, blockIdx.x * 16, red);
 }
 
@@ -528,13 +545,8 @@ __global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArg
     constexpr int ROWS = 16 * RPW;
     __shared__ float red[NW * ROWS * RS];
     const int groups = (d.M + ROWS - 1) / ROWS;
-    if (NV && (int)blockIdx.x >= groups) {  // side work (whole workgroups, before any barrier)
-        const int64_t i = (int64_t)(blockIdx.x - groups) * blockDim.x + threadIdx.x;
-        const int64_t nt = (int64_t)d.side_N * d.side_r;
-        if (i < nt) {
-            const int j = (int)(i / d.side_N), n = (int)(i % d.side_N);
-            d.side_Bt[i] = d.side_B[(int64_t)n * d.side_r + j];
-        }
+    if ((int)blockIdx.x >= groups) {  // side job (whole workgroups, before any barrier)
+        side_transpose(d, blockIdx.x - groups, gridDim.x - groups);
         return;
     }
     const int m0 = blockIdx.x * ROWS;
@@ -665,14 +677,15 @@ __global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArg
     }
 }
 
-// Ranks in passes of up to 64 (each pass reads X again); the side work rides
+// Ranks in passes of up to 64 (each pass reads X again); the side job rides
 // on the first pass.
 template <bool NV>
 static pact_status launch_down_pipe(DownArgs d, hipStream_t st) {
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
         const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
-        const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) + (NV && j0 == 0 ? d.side_wgs : 0))),
+        const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) +
+                                   (j0 == 0 ? side_blocks(d, 64 * kPipeWaves) : 0))),
             block(64 * kPipeWaves);
         d.j0 = j0;
 #define PACT_DOWN_PIPE(RG)                                                                        \
@@ -697,9 +710,10 @@ pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st) {
 
 pact_status launch_lora_down(DownArgs d, hipStream_t st) {
     if (d.p_sk == 1) return launch_down_pipe<false>(d, st);
-    const dim3 grid((unsigned)((d.M + 15) / 16)), block(64 * kDownWaves);
+    const dim3 block(64 * kDownWaves);
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         d.j0 = j0;
+        const dim3 grid((unsigned)((d.M + 15) / 16 + (j0 == 0 ? side_blocks(d, 64 * kDownWaves) : 0)));
         const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
         switch (rg) {
             case 1: hipLaunchKernelGGL(lora_down_kernel<1>, grid, block, 0, st, d); break;
@@ -1460,17 +1474,25 @@ static size_t lora_ws_bytes(int64_t M, int32_t r) {
 static size_t bt_bytes(int64_t N, int32_t r) { return r > 0 ? (size_t)round_up((int64_t)r * N * 2, 256) : 0; }
 
 // Workspace of one projection: the LoRA-down product, the split-K partials of
-// either direction (forward [M][N] over K, input gradient [M][K] over N) and
-// B^T.
+// either direction (forward [M][N] over K, input gradient [M][K] over N), B^T
+// [r][N] and A^T [K][r] (the input gradient's rank operands with contiguous
+// rows).
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     const int cus = device_cus();
     const GemmPlan f = plan_gemm(M, N, K, cus), b = plan_gemm(M, K, N, cus);
     const size_t pf = partial_bytes(M, N, f.ks), pb = partial_bytes(M, K, b.ks);
-    return lora_ws_bytes(M, r) + (pf > pb ? pf : pb) + bt_bytes(N, r);
+    return lora_ws_bytes(M, r) + (pf > pb ? pf : pb) + bt_bytes(N, r) + bt_bytes(K, r);
 }
 
-// Pt [r][Kl] = P^T for P [Kl][r] row-major (the input gradient's B).
-__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t *P, int Kl, int r, uint16_t *Pt) {
+// Pt [r][Kl] = P^T for P [Kl][r] row-major (the input gradient's B) in
+// workgroups [0, ceil(Kl r / 256)), the side job of d in the rest.
+__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t *P, int Kl, int r, uint16_t *Pt,
+                                                             DownArgs d) {
+    const int64_t own = ((int64_t)Kl * r + 255) / 256;
+    if ((int64_t)blockIdx.x >= own) {
+        side_transpose(d, (int64_t)blockIdx.x - own, (int64_t)gridDim.x - own);
+        return;
+    }
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)Kl * r) return;
     const int j = (int)(i / Kl), k = (int)(i % Kl);
@@ -1597,7 +1619,21 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
             }
             for (int g = 0; g <= ng; ++g) a.gcol[g] = groups->col[g];
         }
-        const size_t bt_off = t_bytes + (plan.ks > 1 ? p_bytes : 0);
+        const size_t bt_off = t_bytes + (plan.ks > 1 ? p_bytes : 0), at_off = bt_off + bt_bytes(Kl, r);
+        // LoRA-up operand with strided rows (the input gradient's A [r][Nout]):
+        // A^T [Nout][r] in the workspace, written by side workgroups of the
+        // launch before the epilogue, so the epilogue reads a rank row of 16
+        // bytes per instruction
+        if (q_sn == 1 && q_sj == Nout && ng == 1 && (r & 7) == 0 && ws_bytes >= at_off + bt_bytes(Nout, r)) {
+            uint16_t *At = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + at_off);
+            d.side_B = Qsrc;
+            d.side_Bt = At;
+            d.side_N = r;
+            d.side_r = (int)Nout;
+            Qsrc = At;
+            q_sn = r;
+            q_sj = 1;
+        }
         if (plan.ks > 1 && ng * rpad <= 64) {
             a.down = d;  // computed by workgroups of the split-K main kernel
         } else if (d.p_sk == (int64_t)r && d.p_sj == 1 && M >= 4096 &&
@@ -1605,12 +1641,14 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
             // rank operand with strided rows (the input gradient's B [N][r]):
             // transpose it once so the pipelined LoRA-down reads contiguous rows
             uint16_t *Pt = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(ws) + bt_off);
-            hipLaunchKernelGGL(lora_transpose_kernel, dim3((unsigned)((Kl * r + 255) / 256)), dim3(256), 0, st, Psrc,
-                               (int)Kl, r, Pt);
+            const int own = (int)((Kl * r + 255) / 256);
+            hipLaunchKernelGGL(lora_transpose_kernel, dim3((unsigned)(own + side_blocks(d, 256))), dim3(256), 0, st,
+                               Psrc, (int)Kl, r, Pt, d);
             PACT_TRY(launch_status());
             d.Ps = Pt;
             d.p_sj = Kl;
             d.p_sk = 1;
+            d.side_Bt = nullptr;  // done
             PACT_TRY(launch_lora_down(d, st));
         } else {
             PACT_TRY(launch_lora_down(d, st));

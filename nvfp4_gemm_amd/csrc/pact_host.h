@@ -66,13 +66,17 @@ struct DownArgs {
     // grp_rpad, rank j of block g = j / grp_rpad is row j % grp_rpad (< r) of Pg[g]
     int ngroups, grp_rpad;
     const uint16_t *Pg[4];
-    // extra workgroups of launch_lora_down_nvfp4 (side_wgs of them) write
-    // Bt [side_r][side_N] = B^T (B [side_N][side_r])
-    int side_wgs;
+    // side job (side_Bt != nullptr), run by extra workgroups of the launch
+    // (side_blocks of them): Bt [side_r][side_N] = B^T for B [side_N][side_r]
     const uint16_t *side_B;
     uint16_t *side_Bt;
     int side_N, side_r;
 };
+
+// Workgroups of `threads` threads that the side job of d takes (0: none).
+inline int side_blocks(const DownArgs &d, int threads) {
+    return d.side_Bt ? (int)(((int64_t)d.side_N * d.side_r + threads - 1) / threads) : 0;
+}
 pact_status launch_lora_down(DownArgs d, hipStream_t st);
 pact_status launch_lora_down_nvfp4(DownArgs d, hipStream_t st);
 

@@ -353,7 +353,6 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     dh.side_Bt = Bt;
     dh.side_N = (int)N;
     dh.side_r = r;
-    dh.side_wgs = (int)((N * r + 255) / 256);
     PACT_TRY(launch_lora_down_nvfp4(dh, st));
     // T' = bf16(s dY B): P(j, n) = B^T[j N + n]
     PACT_TRY(launch_lora_down(DownArgs{dY, ld_dy, (int)M, (int)N, Bt, N, 1, r, rpad, 0, lora->scale, Tp}, st));
