@@ -258,7 +258,8 @@ __device__ __forceinline__ void epi_to_tile(float *tile, const float16_t &a, int
 // takes columns 8 (l % 4G) .. +8 of rows l / 4G + 16/G q; C is loaded for all
 // of its rows first, then y = bf16(tile + C) is stored 16 bytes at a time.
 template <int G>
-__device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const float *tile, int mb, int nb0) {
+__device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const float *tile, int mb, int nb0,
+                                         bool have_c = false, const u32x4 *cpre = nullptr) {
     constexpr int LPR = 4 * G;      // lanes per row
     constexpr int RPI = 64 / LPR;   // rows per instruction
     constexpr int NQ = 32 / RPI;    // row steps
@@ -292,8 +293,12 @@ __device__ __forceinline__ void epi_rows(const GemmArgs &p, int lane, const floa
                                                                                (int)p.y_rec, kRsrcWord3);
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(off0 + (uint32_t)q * step), 0, 0);
-                cv[q] = u32x4{v[0], v[1], v[2], v[3]};
+                if (have_c) {
+                    cv[q] = cpre[q];
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(off0 + (uint32_t)q * step), 0, 0);
+                    cv[q] = u32x4{v[0], v[1], v[2], v[3]};
+                }
             }
         }
 #pragma unroll
@@ -357,6 +362,26 @@ __device__ __forceinline__ void static_for(Fn &&f) {
 // issued together, its fragments finished and written to the wavefront's LDS
 // tile (epi_tile_floats<G>() floats, not shared with other wavefronts), then
 // the group is stored row by row.  accf(I) returns fragment I.
+// The C words epi_rows<G> reads on its buffer-descriptor path, loaded ahead
+// of it; false (nothing loaded) for lanes that take the other path.
+template <int G>
+__device__ __forceinline__ bool epi_c_prefetch(const GemmArgs &p, int lane, int mb, int nb0, u32x4 (&cv)[8 / G]) {
+    constexpr int LPR = 4 * G, RPI = 64 / LPR, NQ = 32 / RPI;
+    static_assert(NQ == 8 / G, "row steps");
+    const int rr = lane / LPR, n = nb0 + 8 * (lane % LPR);
+    if (!p.C || !p.y_rec || n + 8 > p.N) return false;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void *)p.C, (short)0, (int)p.y_rec,
+                                                                       kRsrcWord3);
+    const uint32_t off0 = ((uint32_t)(mb + rr) * (uint32_t)p.ldy + (uint32_t)n) * 2u;
+    const uint32_t step = (uint32_t)RPI * (uint32_t)p.ldy * 2u;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(off0 + (uint32_t)q * step), 0, 0);
+        cv[q] = u32x4{v[0], v[1], v[2], v[3]};
+    }
+    return true;
+}
+
 template <int F, int G, typename AccFn>
 __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&accf, const int (&mb)[F],
                                           const int (&nb)[F], float *tile) {
@@ -1369,6 +1394,14 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
     const int lane = threadIdx.x & 63;
     const int fi = w / FN2, fj = 2 * (w - fi * FN2);
     const int64_t fstride = (int64_t)FM * FN * 1024;
+    const int mbs[2] = {32 * fi, 32 * fi}, nbs[2] = {32 * fj, 32 * fj + 32};
+    // the epilogue's operands (row and column scales, LoRA rows, C) are
+    // loaded first, so their latency overlaps that of the partials
+    EpiIn in[2];
+    epi_load(p, mbs[0], nbs[0], lane, in[0]);
+    epi_load(p, mbs[1], nbs[1], lane, in[1]);
+    u32x4 cv[4];
+    const bool cpre = epi_c_prefetch<2>(p, lane, mbs[0], nbs[0], cv);
     float16_t acc[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -1392,9 +1425,16 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
             }
         }
     }
-    const int mbs[2] = {32 * fi, 32 * fi}, nbs[2] = {32 * fj, 32 * fj + 32};
-    epi_frags<2, 2>(p, lane, [&](auto ic) -> float16_t & { return acc[decltype(ic)::value]; }, mbs, nbs,
-                    tiles[threadIdx.x >> 6]);
+    float *tile = tiles[threadIdx.x >> 6];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        epi_finish(p, acc[i], mbs[i], nbs[i], lane, in[i]);
+        epi_to_tile<2>(tile, acc[i], i, lane);
+    }
+    // LDS operations of one wavefront complete in order; the wait keeps the
+    // compiler from treating the tile reads as independent
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    epi_rows<2>(p, lane, tile, mbs[0], nbs[0], cpre, cv);
 }
 
 // ---- launch plan ------------------------------------------------------------

@@ -49,6 +49,7 @@ def _case(M, K, rows, r, seed, rows_sample=None):
     (96, 256, [96, 32, 160, 64], 32),     # four groups, boundaries inside 256-column tiles
     (128, 1024, [512, 128, 128], 32),     # 96 ranks: LoRA-down in two passes
     (64, 256, [256, 64, 64], 0),          # frozen only
+    (100, 4096, [128, 64, 64], 16),       # K split across workgroups
 ])
 def test_grouped_fwd_parity(M, K, rows, r):
     _case(M, K, rows, r, seed=M + K + sum(rows) + r)

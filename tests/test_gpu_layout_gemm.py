@@ -106,10 +106,11 @@ def test_gemm_layer_sizes_sampled_rows(M, N, K, r):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(1024, 512, 2048, 16), (1024, 2048, 8192, 16), (1000, 528, 2048, 8),
-                                     (256, 512, 1024, 8)])
+                                     (256, 512, 1024, 8), (1000, 528, 2048, 5), (1024, 512, 2048, 48)])
 def test_gemm_split_k(M, N, K, r):
     """Shapes whose launch plan splits K across workgroups (FP32 partials
-    summed in split order by a second kernel), including ragged M and N."""
+    summed in split order by a second kernel), including ragged M and N and
+    ranks that are not multiples of 8 or exceed 32."""
     assert max(pb.pact_debug_gemm_plan(M, N, K)[1], pb.pact_debug_gemm_plan(M, K, N)[1]) > 1
     rows = np.unique(np.concatenate([[0, 1, M - 1], np.arange(5, M, max(1, M // 24))]))
     _run_pair(M, N, K, r, seed=17, with_c=True, rows=rows)
