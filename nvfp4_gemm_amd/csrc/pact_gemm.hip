@@ -365,9 +365,9 @@ __device__ __forceinline__ void static_for(Fn &&f) {
 // The C words epi_rows<G> reads on its buffer-descriptor path, loaded ahead
 // of it; false (nothing loaded) for lanes that take the other path.
 template <int G>
-__device__ __forceinline__ bool epi_c_prefetch(const GemmArgs &p, int lane, int mb, int nb0, u32x4 (&cv)[8 / G]) {
+__device__ __forceinline__ bool epi_c_prefetch(const GemmArgs &p, int lane, int mb, int nb0, u32x4 (&cv)[2 * G]) {
     constexpr int LPR = 4 * G, RPI = 64 / LPR, NQ = 32 / RPI;
-    static_assert(NQ == 8 / G, "row steps");
+    static_assert(NQ == 2 * G, "row steps");
     const int rr = lane / LPR, n = nb0 + 8 * (lane % LPR);
     if (!p.C || !p.y_rec || n + 8 > p.N) return false;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void *)p.C, (short)0, (int)p.y_rec,
@@ -1381,30 +1381,36 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
     }, mbs, nbs, reinterpret_cast<float *>(lds) + wave * epi_tile_floats<2>(), split);
 }
 
-// Split-K epilogue: wavefront w takes the two horizontally adjacent output
-// fragments (w / FN2, 2 (w % FN2)) and (w / FN2, 2 (w % FN2) + 1), FN2 =
-// ceil(FN / 2), adds each one's ks partials in split order (s = 0, 1, ...;
-// the same order on every run) and runs the epilogue on the sums.  A second
-// fragment past the output (FN odd) reads nothing and stores nothing.
+// Split-K epilogue: wavefront w takes the G horizontally adjacent output
+// fragments (w / FNG, G (w % FNG) + i), i < G, FNG = ceil(FN / G), adds each
+// one's ks partials in split order (s = 0, 1, ...; the same order on every
+// run) and runs the epilogue on the sums.  A fragment past the output (FN not
+// a multiple of G) reads nothing and stores nothing.
+template <int G>
 __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) float tiles[4][epi_tile_floats<2>()];
-    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5, FN2 = (FN + 1) >> 1;
+    __shared__ __attribute__((aligned(16))) float tiles[4][epi_tile_floats<G>()];
+    const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5, FNG = (FN + G - 1) / G;
     const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (w >= FM * FN2) return;  // whole wavefronts
+    if (w >= FM * FNG) return;  // whole wavefronts
     const int lane = threadIdx.x & 63;
-    const int fi = w / FN2, fj = 2 * (w - fi * FN2);
+    const int fi = w / FNG, fj = G * (w - fi * FNG);
     const int64_t fstride = (int64_t)FM * FN * 1024;
-    const int mbs[2] = {32 * fi, 32 * fi}, nbs[2] = {32 * fj, 32 * fj + 32};
+    int mbs[G], nbs[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        mbs[i] = 32 * fi;
+        nbs[i] = 32 * (fj + i);
+    }
     // the epilogue's operands (row and column scales, LoRA rows, C) are
     // loaded first, so their latency overlaps that of the partials
-    EpiIn in[2];
-    epi_load(p, mbs[0], nbs[0], lane, in[0]);
-    epi_load(p, mbs[1], nbs[1], lane, in[1]);
-    u32x4 cv[4];
-    const bool cpre = epi_c_prefetch<2>(p, lane, mbs[0], nbs[0], cv);
-    float16_t acc[2];
+    EpiIn in[G];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int i = 0; i < G; ++i) epi_load(p, mbs[i], nbs[i], lane, in[i]);
+    u32x4 cv[2 * G];
+    const bool cpre = epi_c_prefetch<G>(p, lane, mbs[0], nbs[0], cv);
+    float16_t acc[G];
+#pragma unroll
+    for (int f = 0; f < G; ++f) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[f][e] = 0.0f;
         if (fj + f >= FN) continue;
@@ -1427,14 +1433,14 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
     }
     float *tile = tiles[threadIdx.x >> 6];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < G; ++i) {
         epi_finish(p, acc[i], mbs[i], nbs[i], lane, in[i]);
-        epi_to_tile<2>(tile, acc[i], i, lane);
+        epi_to_tile<G>(tile, acc[i], i, lane);
     }
     // LDS operations of one wavefront complete in order; the wait keeps the
     // compiler from treating the tile reads as independent
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    epi_rows<2>(p, lane, tile, mbs[0], nbs[0], cpre, cv);
+    epi_rows<G>(p, lane, tile, mbs[0], nbs[0], cpre, cv);
 }
 
 // ---- launch plan ------------------------------------------------------------
@@ -1570,8 +1576,9 @@ static pact_status launch_plan(const GemmArgs &a, int kernel, hipStream_t st) {
     }
     PACT_TRY(launch_status());
     if (a.ks > 1) {
-        const int64_t pairs = ((int64_t)(a.M + 31) / 32) * (((a.N + 31) / 32 + 1) / 2);
-        hipLaunchKernelGGL(splitk_epi_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, a);
+        // one fragment per wavefront: more wavefronts, more loads in flight
+        const int64_t frags = ((int64_t)(a.M + 31) / 32) * ((a.N + 31) / 32);
+        hipLaunchKernelGGL(splitk_epi_kernel<1>, dim3((unsigned)((frags + 3) / 4)), dim3(256), 0, st, a);
         PACT_TRY(launch_status());
     }
     return PACT_OK;
