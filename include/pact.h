@@ -277,12 +277,17 @@ pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64_t n, void 
 pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *stream);
 
 /* Diagnostic: the launch plan of a GEMM with output [M][N] contracted over K
- * on the current device (host only, no GPU work): *kernel = 0 for the
- * 256 x 256 single-decode kernel, 1-4 for the main kernel with wavefronts
- * (2,2,1), (2,1,2), (1,2,2), (1,1,4); *ks = number of K ranges split across
- * workgroups (1: no split).  PACT_ERR_INVALID_ARG for negative sizes or null
- * outputs. */
-pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t *kernel, int32_t *ks);
+ * with LoRA rank r (0: none) on the current device, as pact_gemm_nvfp4_fwd
+ * (dgrad == 0) or pact_gemm_nvfp4_dgrad (dgrad != 0) chooses it given the
+ * full workspace (host only, no GPU work): *kernel = 0 for the 256 x 256
+ * single-decode kernel, 1-4 for the main kernel with wavefronts (2,2,1),
+ * (2,1,2), (1,2,2), (1,1,4); *ks = number of K ranges split across
+ * workgroups (1: no split); *fused (may be NULL) = 1 when the LoRA-down runs
+ * as workgroups of the split-K launch, 0 when it runs as a launch of its
+ * own.  PACT_ERR_INVALID_ARG for negative sizes, r outside 0..256 or null
+ * kernel / ks. */
+pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad, int32_t *kernel,
+                                 int32_t *ks, int32_t *fused);
 
 #ifdef __cplusplus
 }

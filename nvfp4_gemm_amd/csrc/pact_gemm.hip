@@ -1450,6 +1450,7 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
 struct GemmPlan {
     int kernel;
     int ks;
+    bool fuse;  // the LoRA-down runs as a row of workgroups of the split-K launch
 };
 
 struct KernelShape {
@@ -1489,9 +1490,76 @@ static double plan_cost(int64_t M, int64_t N, int64_t K, int kernel, int ks, int
     return t;
 }
 
-static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cus) {
+// The LoRA-down product [M][Kl] x [Kl][rpad] of a GEMM: as a launch of its
+// own before the GEMM, bound by reading X (BF16) from HBM; or fused into a
+// split-K launch as one workgroup per output tile taking ceil(row groups /
+// tiles) groups of 16 rows each (measured: about 1 us plus 1.9 us per 1024
+// of Kl per group, 30% more with strided rank-operand rows).  A fused row
+// occupies its CUs that long: the GEMM workgroups are list-scheduled onto
+// the CUs after the busy down workgroups and the delay of the last one over
+// the down-free schedule is the fused plan's extra cost.
+struct DownPlan {
+    int64_t kl;    // LoRA input width (0: no LoRA)
+    bool strided;  // rank-operand rows strided (the input gradient's B)
+    int rpad;      // ranks, rounded up to 16
+};
+
+// A launch of its own: one workgroup per 16 (32 from 4096) rows walks all of
+// Kl (measured at 1024 rows: 3 us plus 2.0 us per 1024 of Kl with the
+// pipelined kernel, 2.75 us with the 16-wavefront kernel that reads strided
+// rank-operand rows below 4096 rows; from 4096 rows strided rows are first
+// transposed, a launch of about 3 us), or the BF16 read of X at 3 TB/s when
+// that is longer.
+static double down_alone_us(int64_t M, const DownPlan &dp) {
+    const double kk = (double)dp.kl / 1024.0, ranks = 1.0 + 0.25 * (dp.rpad / 16 - 1);
+    const bool wide = M >= 4096, slow = dp.strided && !wide;
+    const double rounds = (double)((M + (wide ? 32 : 16) * 256 - 1) / ((wide ? 32 : 16) * 256));
+    const double lat = 3.0 + rounds * kk * (slow ? 2.75 : 2.0) * (wide ? 1.5 : 1.0) * ranks;
+    const double bw = 3.0 + (double)M * (double)dp.kl * 2.0 / 3.0e6;
+    return (lat > bw ? lat : bw) + (dp.strided && wide ? 3.0 : 0.0);
+}
+
+static double down_fused_extra_us(int64_t M, int64_t N, int kernel, int ks, int cus, double t_main,
+                                  const DownPlan &dp) {
+    const KernelShape &k = kKernels[kernel];
+    const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn), wgs = tiles * ks;
+    const int64_t groups = (M + 15) / 16, busy = groups < tiles ? (groups < cus ? groups : cus) : (tiles < cus ? tiles : cus);
+    const int64_t per = (groups + tiles - 1) / tiles;
+    const double t_down = (double)per * (1.0 + 1.9 * (double)dp.kl / 1024.0) * (dp.strided ? 1.3 : 1.0) *
+                          (1.0 + 0.25 * (dp.rpad / 16 - 1));
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const double t_wg = t_main / (double)rounds;
+    // cus - busy CUs complete a GEMM workgroup at every multiple of t_wg, the
+    // busy ones at t_down + multiples of t_wg; the launch ends at the first
+    // such time by which all wgs can have completed
+    const int64_t F = cus - busy, B = busy;
+    auto done_by = [&](double T) {
+        const int64_t a = (int64_t)(T / t_wg + 1e-9);
+        const int64_t b = T > t_down ? (int64_t)((T - t_down) / t_wg + 1e-9) : 0;
+        return F * a + B * b;
+    };
+    double end = 1e300;
+    if (F > 0)
+        for (int64_t a = 1; a <= wgs / F + 1; ++a)
+            if (done_by(a * t_wg) >= wgs) {
+                end = a * t_wg;
+                break;
+            }
+    if (B > 0)
+        for (int64_t b = 1; b <= wgs / B + 1; ++b)
+            if (t_down + b * t_wg < end && done_by(t_down + b * t_wg) >= wgs) {
+                end = t_down + b * t_wg;
+                break;
+            }
+    if (end > 1e299) end = t_down + (double)rounds * t_wg;
+    if (end < t_down) end = t_down;  // the down workgroups themselves
+    const double base = (double)rounds * t_wg;
+    return end > base ? end - base : 0.0;
+}
+
+static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cus, const DownPlan &dp = {0, false, 16}) {
     const int64_t ns = (K + kSK - 1) / kSK;
-    GemmPlan best = {1, 1};
+    GemmPlan best = {1, 1, false};
     double best_cost = 1e300;
     for (int kernel = 0; kernel < 5; ++kernel) {
         if (kernel == 0 && K % kSK != 0) continue;
@@ -1501,9 +1569,26 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cus) {
             if (ns % ((int64_t)wk * ks) != 0) continue;
             if (ks > 1 && ns / ((int64_t)wk * ks) < 2) continue;  // at least two stages per wavefront
             const double c = plan_cost(M, N, K, kernel, ks, cus);
-            if (c < best_cost) {
-                best_cost = c;
-                best = {kernel, ks};
+            double total = c;
+            bool fuse = false;
+            if (dp.kl > 0) {
+                total = c + down_alone_us(M, dp);
+                // strided rank-operand rows: fused only at one row group per
+                // workgroup (longer ones contend with the GEMM's loads)
+                const KernelShape &kk = kKernels[kernel];
+                const int64_t tiles = ((M + kk.bm - 1) / kk.bm) * ((N + kk.bn - 1) / kk.bn);
+                if (ks > 1 && dp.rpad <= 64 && (!dp.strided || (M + 15) / 16 <= tiles)) {
+                    const double t_main = c - (2.0 * (double)partial_bytes(M, N, ks) / (kPartialTBs * 1e6) + kSplitEpiUs);
+                    const double fused = c + down_fused_extra_us(M, N, kernel, ks, cus, t_main, dp);
+                    if (fused <= total) {
+                        total = fused;
+                        fuse = true;
+                    }
+                }
+            }
+            if (total < best_cost) {
+                best_cost = total;
+                best = {kernel, ks, fuse};
             }
         }
     }
@@ -1525,7 +1610,9 @@ static size_t bt_bytes(int64_t N, int32_t r) { return r > 0 ? (size_t)round_up((
 // rows).
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     const int cus = device_cus();
-    const GemmPlan f = plan_gemm(M, N, K, cus), b = plan_gemm(M, K, N, cus);
+    const int rp = (int)round_up(r > 0 ? r : 16, 16);
+    const GemmPlan f = plan_gemm(M, N, K, cus, DownPlan{r > 0 ? K : 0, false, rp}),
+                   b = plan_gemm(M, K, N, cus, DownPlan{r > 0 ? N : 0, true, rp});
     const size_t pf = partial_bytes(M, N, f.ks), pb = partial_bytes(M, K, b.ks);
     return lora_ws_bytes(M, r) + (pf > pb ? pf : pb) + bt_bytes(N, r) + bt_bytes(K, r);
 }
@@ -1647,9 +1734,13 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
     }
     // K split across workgroups when the plan asks for it and the workspace
     // holds the partials (after the LoRA-down product); otherwise one pass
-    GemmPlan plan = plan_gemm(M, Nout, Kc, device_cus());
+    GemmPlan plan = plan_gemm(M, Nout, Kc, device_cus(),
+                              DownPlan{r > 0 ? Kl : 0, p_sk != 1, ng * (int)round_up(r > 0 ? r : 16, 16)});
     const size_t p_bytes = partial_bytes(M, Nout, plan.ks);
-    if (plan.ks > 1 && (!ws || !aligned16(ws) || ws_bytes < t_bytes + p_bytes)) plan.ks = 1;
+    if (plan.ks > 1 && (!ws || !aligned16(ws) || ws_bytes < t_bytes + p_bytes)) {
+        plan.ks = 1;
+        plan.fuse = false;
+    }
     a.ks = plan.ks;
     a.part = plan.ks > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + t_bytes) : nullptr;
     if (r > 0) {
@@ -1681,7 +1772,7 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
             q_sn = r;
             q_sj = 1;
         }
-        if (plan.ks > 1 && ng * rpad <= 64) {
+        if (plan.fuse && plan.ks > 1 && ng * rpad <= 64) {
             a.down = d;  // computed by workgroups of the split-K main kernel
         } else if (d.p_sk == (int64_t)r && d.p_sj == 1 && M >= 4096 &&
                    ws_bytes >= bt_off + bt_bytes(Kl, r)) {
@@ -1715,11 +1806,14 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
 
 using namespace pact;
 
-extern "C" pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t *kernel, int32_t *ks) {
-    if (M < 0 || N < 0 || K < 0 || !kernel || !ks) return PACT_ERR_INVALID_ARG;
-    const GemmPlan plan = plan_gemm(M, N, K, device_cus());
+extern "C" pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad,
+                                            int32_t *kernel, int32_t *ks, int32_t *fused) {
+    if (M < 0 || N < 0 || K < 0 || r < 0 || r > 256 || !kernel || !ks) return PACT_ERR_INVALID_ARG;
+    const GemmPlan plan =
+        plan_gemm(M, N, K, device_cus(), DownPlan{r > 0 ? K : 0, dgrad != 0, (int)round_up(r > 0 ? r : 16, 16)});
     *kernel = plan.kernel;
     *ks = plan.ks;
+    if (fused) *fused = plan.fuse ? 1 : 0;
     return PACT_OK;
 }
 

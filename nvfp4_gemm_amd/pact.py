@@ -97,7 +97,8 @@ def lib():
         L.pact_debug_dsilu32.restype = st
         L.pact_debug_dsilu32.argtypes = [P, P, I64, P]
         L.pact_debug_gemm_plan.restype = st
-        L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_int32),
+        L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
         _lib = L
     return _lib
@@ -399,8 +400,11 @@ def pact_debug_sigmoid32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
-def pact_debug_gemm_plan(M: int, N: int, K: int) -> tuple[int, int]:
-    """(kernel, ks) of the GEMM launch plan for output [M][N] over K."""
-    k, ks = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().pact_debug_gemm_plan(M, N, K, ctypes.byref(k), ctypes.byref(ks)), "pact_debug_gemm_plan")
-    return k.value, ks.value
+def pact_debug_gemm_plan(M: int, N: int, K: int, r: int = 0, dgrad: bool = False) -> tuple[int, int, bool]:
+    """(kernel, ks, fused) of the GEMM launch plan for output [M][N] over K
+    with LoRA rank r, as the forward (dgrad False) or input-gradient entry
+    point chooses it; fused: the LoRA-down runs inside the split-K launch."""
+    k, ks, f = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pact_debug_gemm_plan(M, N, K, r, 1 if dgrad else 0, ctypes.byref(k), ctypes.byref(ks),
+                                      ctypes.byref(f)), "pact_debug_gemm_plan")
+    return k.value, ks.value, bool(f.value)

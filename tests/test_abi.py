@@ -124,20 +124,37 @@ def test_gemm_plan_host_logic(L):
     """The launch plan (host logic, no GPU work): large outputs run in one
     pass; a small output with long K splits K, and the workspace query then
     covers the FP32 partials of either direction."""
-    k, ks = ctypes.c_int32(), ctypes.c_int32()
-    assert L.pact_debug_gemm_plan(-1, 8, 8, ctypes.byref(k), ctypes.byref(ks)) == 1
-    assert L.pact_debug_gemm_plan(8, 8, 8, None, ctypes.byref(ks)) == 1
-    assert L.pact_debug_gemm_plan(8192, 8192, 3072, ctypes.byref(k), ctypes.byref(ks)) == 0
+    k, ks, fu = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert L.pact_debug_gemm_plan(-1, 8, 8, 0, 0, ctypes.byref(k), ctypes.byref(ks), None) == 1
+    assert L.pact_debug_gemm_plan(8, 8, 8, 0, 0, None, ctypes.byref(ks), None) == 1
+    assert L.pact_debug_gemm_plan(8, 8, 8, 300, 0, ctypes.byref(k), ctypes.byref(ks), None) == 1
+    assert L.pact_debug_gemm_plan(8192, 8192, 3072, 0, 0, ctypes.byref(k), ctypes.byref(ks), None) == 0
     assert ks.value == 1
-    assert L.pact_debug_gemm_plan(1024, 512, 2048, ctypes.byref(k), ctypes.byref(ks)) == 0
-    assert ks.value > 1 and 0 <= k.value <= 4
+    assert L.pact_debug_gemm_plan(1024, 512, 2048, 0, 0, ctypes.byref(k), ctypes.byref(ks), ctypes.byref(fu)) == 0
+    assert ks.value > 1 and 0 <= k.value <= 4 and fu.value == 0
     split = ks.value
     parts = split * (1024 // 32) * (512 // 32) * 4096
     assert L.pact_gemm_workspace(1024, 512, 2048, 0) >= parts
     assert L.pact_gemm_workspace(1024, 512, 2048, 16) >= parts + 2 * 16 * 1024
     assert L.pact_gemm_workspace(1024, 2048, 512, 16) >= parts + 2 * 16 * 1024  # the input-gradient direction
-    assert L.pact_debug_gemm_plan(100, 200, 520, ctypes.byref(k), ctypes.byref(ks)) == 0
+    assert L.pact_debug_gemm_plan(100, 200, 520, 0, 0, ctypes.byref(k), ctypes.byref(ks), None) == 0
     assert ks.value == 1  # K % 64 != 0: no split
+
+
+def test_gemm_plan_lora_down_placement(L):
+    """The LoRA-down of a split-K GEMM runs inside the split launch only where
+    its workgroups do not hold back the GEMM's: a few short rows fit beside the
+    GEMM workgroups; at 4096 tokens over 8960 columns (three row groups per
+    down workgroup) the input gradient's strided down runs as a launch of its
+    own, and a fused forward down needs a split deep enough (ks > 2) that the
+    GEMM's second round absorbs it."""
+    k, ks, fu = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert L.pact_debug_gemm_plan(1024, 512, 2048, 16, 0, ctypes.byref(k), ctypes.byref(ks), ctypes.byref(fu)) == 0
+    assert ks.value > 1 and fu.value == 1
+    assert L.pact_debug_gemm_plan(4096, 1536, 8960, 16, 1, ctypes.byref(k), ctypes.byref(ks), ctypes.byref(fu)) == 0
+    assert fu.value == 0
+    assert L.pact_debug_gemm_plan(4096, 1536, 8960, 16, 0, ctypes.byref(k), ctypes.byref(ks), ctypes.byref(fu)) == 0
+    assert fu.value == 0 or ks.value > 2
 
 
 def test_backward_validation(L):

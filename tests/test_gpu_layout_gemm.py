@@ -111,7 +111,7 @@ def test_gemm_split_k(M, N, K, r):
     """Shapes whose launch plan splits K across workgroups (FP32 partials
     summed in split order by a second kernel), including ragged M and N and
     ranks that are not multiples of 8 or exceed 32."""
-    assert max(pb.pact_debug_gemm_plan(M, N, K)[1], pb.pact_debug_gemm_plan(M, K, N)[1]) > 1
+    assert max(pb.pact_debug_gemm_plan(M, N, K, r)[1], pb.pact_debug_gemm_plan(M, K, N, r, True)[1]) > 1
     rows = np.unique(np.concatenate([[0, 1, M - 1], np.arange(5, M, max(1, M // 24))]))
     _run_pair(M, N, K, r, seed=17, with_c=True, rows=rows)
 
@@ -120,7 +120,7 @@ def test_gemm_split_k_workspace_fallback():
     """A workspace holding only the LoRA-down product runs the GEMM in one
     pass; both paths meet the tolerance and each is deterministic."""
     M, N, K, r = 1024, 512, 2048, 16
-    assert pb.pact_debug_gemm_plan(M, N, K)[1] > 1
+    assert pb.pact_debug_gemm_plan(M, N, K, r)[1] > 1
     li = synth.single_linear_inputs(M=M, N=N, K=K, r=r, seed=23, act="t4", outliers=True)
     A, B, lora = _lora(li, r)
     rows = np.unique(np.concatenate([[0, M - 1], np.arange(3, M, 41)]))
