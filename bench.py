@@ -221,13 +221,16 @@ class Stack:
         c = []
 
         def grads(nm, xq, dY, L, l):
-            """dA, dB of projection nm of layer l (input xq from the stash, output gradient dY)."""
+            """dA, dB of projection nm of layer l (input xq from the stash, output gradient dY),
+            right after the projection's input-gradient GEMM: its workspace still holds
+            T' = bf16(s dY B), which the gradient call takes instead of computing it."""
             if not self.lora_grads:
                 return
             n, k = S.projections()[nm]
             c.append(("lora_grads", 0, nvb(M, k) + 2 * M * n + 2 * r * (n + k) + 4 * r * (n + k),
                       lambda nm=nm, xq=xq, dY=dY, L=L, l=l: pb.pact_lora_grads_nvfp4(
-                          xq, dY, L[nm], dA=self.gA[l][nm], dB=self.gB[l][nm], ws=self.gws), 4 * M * r * (n + k)))
+                          xq, dY, L[nm], dA=self.gA[l][nm], dB=self.gB[l][nm], ws=self.gws, T_dy=ws),
+                      4 * M * r * (n + k)))
         xin = lambda l: self.xs[0] if l == 0 else self.xs[1 + (l - 1) % 2]
         xout = lambda l: self.xs[1 + l % 2]
         for l in range(self.L):
@@ -299,12 +302,12 @@ class Stack:
             c.append(("quantize", 0, M * KV * 2 + nvb(M, KV), lambda dv=dv: pb.pact_quantize_nvfp4(dv, self.dvq), 0))
             c.append(("gemm_dgrad", gemm_fl(H, H), 0, lambda dq=dq, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dqq, Wb["q"], dY=dq, lora=L["q"], dX=self.dn, ws=ws), lora_fl(H, H)))
+            grads("q", st["n1q"], dq, L, l)
             c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dk=dk, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dkq, Wb["k"], dY=dk, lora=L["k"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
+            grads("k", st["n1q"], dk, L, l)
             c.append(("gemm_dgrad", gemm_fl(KV, H), 0, lambda dv=dv, L=L, Wb=Wb: pb.pact_gemm_nvfp4_dgrad(
                 self.dvq, Wb["v"], dY=dv, lora=L["v"], C=self.dn, dX=self.dn, ws=ws), lora_fl(KV, H)))
-            grads("q", st["n1q"], dq, L, l)
-            grads("k", st["n1q"], dk, L, l)
             grads("v", st["n1q"], dv, L, l)
             last = j == self.L - 1
             c.append(("rmsnorm_bwd", 0, M * H * 2 + nvb(M, H) + 4 * M + M * H * 2 + M * H * 2

@@ -247,9 +247,13 @@ size_t pact_lora_grads_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
  * B [N][r], scale s; dA [r][K] and dB [N][r] FP32, row-major.  K % 16 == 0,
  * N % 16 == 0, 1 <= r <= 64.  Empty M gives zero gradients.  The workspace
  * (pact_lora_grads_workspace bytes) holds T^, T', B^T and partial sums; X^ is
- * decoded in registers, never stored. */
+ * decoded in registers, never stored.  T_dy (may be NULL; 16-byte aligned):
+ * T' [M][round_up(r, 16)] BF16 already computed, such as the first bytes of
+ * the workspace of a pact_gemm_nvfp4_dgrad call with the same dY and lora
+ * (its LoRA-down product, stream-ordered before this call and not yet
+ * overwritten); the entry point then does not compute T'. */
 pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int64_t ld_dy, int64_t N,
-                                  const pact_lora *lora, float *dA, float *dB, void *ws,
+                                  const pact_lora *lora, const uint16_t *T_dy, float *dA, float *dB, void *ws,
                                   size_t ws_bytes, void *stream);
 
 /* One AdamW step of the trainable adapters over a flat buffer of n FP32

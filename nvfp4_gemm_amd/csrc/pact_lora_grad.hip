@@ -301,8 +301,8 @@ extern "C" size_t pact_lora_grads_workspace(int64_t M, int64_t N, int64_t K, int
 }
 
 extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int64_t ld_dy, int64_t N,
-                                             const pact_lora *lora, float *dA, float *dB, void *ws,
-                                             size_t ws_bytes, void *stream) {
+                                             const pact_lora *lora, const uint16_t *T_dy, float *dA, float *dB,
+                                             void *ws, size_t ws_bytes, void *stream) {
     if (!Xq || !lora || !lora->A || !lora->B || !dA || !dB) return PACT_ERR_INVALID_ARG;
     const int64_t M = Xq->rows, K = Xq->cols;
     const int r = lora->r;
@@ -312,6 +312,7 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     PACT_TRY(check_nvfp4(Xq, M, K));
     PACT_TRY(check_bf16(dY, ld_dy, N));
     if (!aligned16(lora->A) || !aligned16(lora->B) || !aligned16(dA) || !aligned16(dB)) return PACT_ERR_MISALIGNED;
+    if (T_dy && !aligned16(T_dy)) return PACT_ERR_MISALIGNED;
     hipStream_t st = as_stream(stream);
     if (M == 0 || K == 0 || N == 0) {  // empty sums: zero gradients
         if (K * r > 0)
@@ -334,7 +335,7 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     float *partB = reinterpret_cast<float *>(base);
     float *partA = reinterpret_cast<float *>(base + grad_part_bytes(M, N, r, false));
     // T^ = bf16(s X^ A^T) straight from the NVFP4 rows (P(j, k) = A[j K + k]);
-    // its side workgroups write B^T
+    // unless T' is given, its side workgroups write B^T for T'
     DownArgs dh{};
     dh.ldx = K;
     dh.M = (int)M;
@@ -349,13 +350,16 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     dh.xc = Xq->codes;
     dh.xs = Xq->scales;
     dh.xd = Xq->row_scale;
-    dh.side_B = lora->B;
-    dh.side_Bt = Bt;
-    dh.side_N = (int)N;
-    dh.side_r = r;
+    if (!T_dy) {
+        dh.side_B = lora->B;
+        dh.side_Bt = Bt;
+        dh.side_N = (int)N;
+        dh.side_r = r;
+    }
     PACT_TRY(launch_lora_down_nvfp4(dh, st));
     // T' = bf16(s dY B): P(j, n) = B^T[j N + n]
-    PACT_TRY(launch_lora_down(DownArgs{dY, ld_dy, (int)M, (int)N, Bt, N, 1, r, rpad, 0, lora->scale, Tp}, st));
+    if (!T_dy)
+        PACT_TRY(launch_lora_down(DownArgs{dY, ld_dy, (int)M, (int)N, Bt, N, 1, r, rpad, 0, lora->scale, Tp}, st));
     // dB[n][j] = sum_m dY[m][n] T^[m][j];  dA[j][k] = sum_m T'[m][j] X^[m][k];
     // dB's split reduction runs beside dA's contraction, dA's on its own
     pact_status stt = PACT_OK;
@@ -374,7 +378,7 @@ extern "C" pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_
     ga.vc = Xq->codes;
     ga.vs = Xq->scales;
     ga.vd = Xq->row_scale;
-    ga.T = Tp;
+    ga.T = T_dy ? T_dy : Tp;
     ga.ldt = rpad;
     ga.M = (int)M;
     ga.C = (int)K;

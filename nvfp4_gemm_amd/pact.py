@@ -88,7 +88,7 @@ def lib():
         L.pact_lora_grads_workspace.restype = ctypes.c_size_t
         L.pact_lora_grads_workspace.argtypes = [I64, I64, I64, ctypes.c_int32]
         L.pact_lora_grads_nvfp4.restype = st
-        L.pact_lora_grads_nvfp4.argtypes = [NV, P, I64, I64, LO, P, P, P, ctypes.c_size_t, P]
+        L.pact_lora_grads_nvfp4.argtypes = [NV, P, I64, I64, LO, P, P, P, P, ctypes.c_size_t, P]
         L.pact_gemm_nvfp4_fwd_grouped.restype = st
         L.pact_gemm_nvfp4_fwd_grouped.argtypes = [NV, P, I64, NV, ctypes.c_int32, ctypes.POINTER(I64),
                                                   LO, P, I64, P, ctypes.c_size_t, P]
@@ -358,9 +358,11 @@ def pact_lora_grads_workspace(M: int, N: int, K: int, r: int) -> int:
     return int(lib().pact_lora_grads_workspace(M, N, K, r))
 
 
-def pact_lora_grads_nvfp4(Xq: NVFP4Tensor, dY, lora: LoRA, dA=None, dB=None, ws=None, stream=None):
+def pact_lora_grads_nvfp4(Xq: NVFP4Tensor, dY, lora: LoRA, dA=None, dB=None, ws=None, stream=None, T_dy=None):
     """dB = dY^T bf16(s X^ A^T) [N, r] and dA = bf16(s dY B)^T X^ [r, K], FP32,
-    with X^ the BF16 values of the stashed NVFP4 input."""
+    with X^ the BF16 values of the stashed NVFP4 input.  T_dy: bf16(s dY B)
+    already computed ([M][round_up(r, 16)] BF16 at its start, e.g. the
+    workspace of the input-gradient GEMM of the same dY and lora), or None."""
     M, N = dY.shape
     K, r = Xq.cols, lora.r
     if dA is None:
@@ -370,8 +372,11 @@ def pact_lora_grads_nvfp4(Xq: NVFP4Tensor, dY, lora: LoRA, dA=None, dB=None, ws=
     if ws is None:
         ws = torch.empty((max(pact_lora_grads_workspace(M, N, K, r), 16),), dtype=torch.uint8, device=dY.device)
     dx, dl = Xq.desc(), lora.desc()
-    _check(lib().pact_lora_grads_nvfp4(ctypes.byref(dx), _ptr(dY), _ld(dY), N, ctypes.byref(dl), _ptr(dA),
-                                       _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)), "pact_lora_grads_nvfp4")
+    if T_dy is not None:
+        assert T_dy.device == dY.device and T_dy.numel() * T_dy.element_size() >= M * ((r + 15) // 16 * 16) * 2
+    _check(lib().pact_lora_grads_nvfp4(ctypes.byref(dx), _ptr(dY), _ld(dY), N, ctypes.byref(dl), _ptr(T_dy),
+                                       _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
+           "pact_lora_grads_nvfp4")
     return dA, dB
 
 

@@ -193,13 +193,14 @@ def test_lora_grads_validation(L):
     need = L.pact_lora_grads_workspace(M, N, K, r)
     assert need >= 2 * M * 16 * 2                                             # holds T^ and T'
     assert L.pact_lora_grads_workspace(M, N, K, 0) == 0
-    assert f(ctypes.byref(q), FAKE, N, N, None, FAKE, FAKE, FAKE, need, None) == 1        # no adapter
+    assert f(ctypes.byref(q), FAKE, N, N, None, None, FAKE, FAKE, FAKE, need, None) == 1        # no adapter
     big = pb.pact_lora(FAKE, FAKE, 65, 2.0)
-    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(big), FAKE, FAKE, FAKE, need, None) == 2  # r > 64
-    assert f(ctypes.byref(q), FAKE, N, 24, ctypes.byref(lo), FAKE, FAKE, FAKE, need, None) == 2  # N % 16
-    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE + 4, FAKE, FAKE, need, None) == 3  # dA
-    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need - 1, None) == 4  # workspace
-    assert f(ctypes.byref(q), FAKE, N - 8, N, ctypes.byref(lo), FAKE, FAKE, FAKE, need, None) == 1  # ld < N
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(big), None, FAKE, FAKE, FAKE, need, None) == 2  # r > 64
+    assert f(ctypes.byref(q), FAKE, N, 24, ctypes.byref(lo), None, FAKE, FAKE, FAKE, need, None) == 2  # N % 16
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), None, FAKE + 4, FAKE, FAKE, need, None) == 3  # dA
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), FAKE + 4, FAKE, FAKE, FAKE, need, None) == 3  # T'
+    assert f(ctypes.byref(q), FAKE, N, N, ctypes.byref(lo), None, FAKE, FAKE, FAKE, need - 1, None) == 4  # workspace
+    assert f(ctypes.byref(q), FAKE, N - 8, N, ctypes.byref(lo), None, FAKE, FAKE, FAKE, need, None) == 1  # ld < N
 
 
 def test_adamw_validation(L):

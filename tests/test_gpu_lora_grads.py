@@ -81,7 +81,7 @@ def test_lora_grads_no_tokens():
     desc = pb.pact_nvfp4(q.codes.data_ptr(), q.scales.data_ptr(), q.row_scale.data_ptr(), 0, 32)
     lo = pb.pact_lora(A.data_ptr(), B.data_ptr(), 4, 2.0)
     assert L.pact_lora_grads_nvfp4(ctypes.byref(desc), ctypes.c_void_p(dY.data_ptr()), 16, 16, ctypes.byref(lo),
-                                   ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()), None, 0,
+                                   None, ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()), None, 0,
                                    None) == 0
     torch.cuda.synchronize()
     assert torch.all(dA == 0) and torch.all(dB == 0)
@@ -101,3 +101,22 @@ def test_lora_grads_strided_dy():
     torch.cuda.synchronize()
     _check(gdA, dA, "dA strided dY")
     _check(gdB, dB, "dB strided dY")
+
+
+@pytest.mark.parametrize("M,N,K,r", [(300, 512, 256, 16), (1024, 2048, 8192, 16), (4096, 1536, 1536, 16)])
+def test_lora_grads_with_dgrad_t(M, N, K, r):
+    """T' = bf16(s dY B) taken from the workspace of the input-gradient GEMM
+    of the same dY and adapter (its LoRA-down product) instead of computed
+    again: the gradients meet the same bound against the oracle."""
+    xq, dY, A, B = _case(M, N, K, r, seed=M + 5 * N + K)
+    dA, dB = oracle.lora_grads(xq, dY, A, B, 2.0)
+    lora = pb.LoRA(G.dev_bf16(A), G.dev_bf16(B), 2.0)
+    gdY = G.dev_bf16(dY)
+    W = synth.weight_bf16(np.random.default_rng(M), N, K)
+    _, wb = pb.pact_build_weight_layouts(G.dev_bf16(W))
+    ws = torch.empty((pb.pact_gemm_workspace(M, N, K, r),), dtype=torch.uint8, device="cuda")
+    pb.pact_gemm_nvfp4_dgrad(pb.pact_quantize_nvfp4(gdY), wb, dY=gdY, lora=lora, ws=ws)
+    gdA, gdB = pb.pact_lora_grads_nvfp4(G.dev_nvfp4(xq), gdY, lora, T_dy=ws)
+    torch.cuda.synchronize()
+    _check(gdA, dA, f"dA {M}x{N}x{K} with the GEMM's T'")
+    _check(gdB, dB, f"dB {M}x{N}x{K} with the GEMM's T'")
