@@ -28,6 +28,7 @@
 // The LoRA-down product T = bf16(s X A^T) is a separate small kernel; the
 // LoRA-up product T Q^T is accumulated by BF16 MFMAs into the row-scaled
 // accumulators in the epilogue.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -1523,8 +1524,9 @@ static double down_fused_extra_us(int64_t M, int64_t N, int kernel, int ks, int 
                                   const DownPlan &dp) {
     const KernelShape &k = kKernels[kernel];
     const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn), wgs = tiles * ks;
-    const int64_t groups = (M + 15) / 16, busy = groups < tiles ? (groups < cus ? groups : cus) : (tiles < cus ? tiles : cus);
-    const int64_t per = (groups + tiles - 1) / tiles;
+    const int64_t groups = (M + 15) / 16;
+    const int64_t busy = std::min<int64_t>(std::min(groups, tiles), cus);  // down workgroups with rows
+    const int64_t per = (groups + tiles - 1) / tiles;                      // row groups each
     const double t_down = (double)per * (1.0 + 1.9 * (double)dp.kl / 1024.0) * (dp.strided ? 1.3 : 1.0) *
                           (1.0 + 0.25 * (dp.rpad / 16 - 1));
     const int64_t rounds = (wgs + cus - 1) / cus;
