@@ -552,21 +552,19 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
 // (p_sk == 1).  Its cost is the number of vector memory instructions in
 // flight per CU, and the rank operand P costs as many instructions as X (it is
 // read from L2 by every row group).  So: a wavefront takes RPW row groups and
-// uses every P fragment for all of them; NW = 4 wavefronts split K; each
+// uses every P fragment for all of them; NW = 8 or 16 wavefronts split K
+// (enough wavefronts in flight even when the row groups are few); each
 // wavefront works through its K range in stages of 128 K with the loads of
 // the next stage issued before the MFMAs of the current one (branch-free: out
 // of range fragments read a clamped address and are zeroed).  Within a stage,
 // fragment c of lane group g covers 8 K at kpos(c, g): for BF16 rows a
 // row's 64 contiguous bytes per instruction; for NVFP4 rows the lane's 16
 // code bytes hold its 32 K (decoded to BF16 in registers).
-constexpr int kPipeWaves = 4;
-
 template <bool NV>
 __device__ __forceinline__ int down_kpos(int c, int g) { return NV ? 32 * g + 8 * c : 32 * c + 8 * g; }
 
-template <int RG, int RPW, bool NV>
-__global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArgs d) {
-    constexpr int NW = kPipeWaves;
+template <int RG, int RPW, bool NV, int NW>
+__global__ __launch_bounds__(64 * NW) void lora_down_pipe_kernel(DownArgs d) {
     constexpr int RS = 16 * RG + 1;
     constexpr int ROWS = 16 * RPW;
     __shared__ float red[NW * ROWS * RS];
@@ -703,6 +701,31 @@ __global__ __launch_bounds__(64 * kPipeWaves) void lora_down_pipe_kernel(DownArg
     }
 }
 
+// Wavefronts per workgroup of the pipelined LoRA-down: 16 when row groups are
+// few (so that enough loads are in flight) and a wavefront's fragments fit
+// 128 VGPRs (one or two rank-by-row groups); 4 for 4 rank groups of two row
+// groups (its fragments take up to 256 VGPRs); 8 otherwise.  Every choice is
+// free of register spills.
+static int pipe_waves(int rg, int rpw, int groups) {
+    if (rg * rpw <= 2 && groups <= 128) return 16;
+    if (rg == 4 && rpw == 2) return 4;
+    return 8;
+}
+
+template <int RG, int RPW, bool NV>
+static void launch_pipe_nw(int nw, dim3 grid, dim3 block, hipStream_t st, const DownArgs &d) {
+    if constexpr (RG * RPW <= 2) {
+        if (nw == 16) {
+            hipLaunchKernelGGL((lora_down_pipe_kernel<RG, RPW, NV, 16>), grid, block, 0, st, d);
+            return;
+        }
+    }
+    if constexpr (RG == 4 && RPW == 2)
+        hipLaunchKernelGGL((lora_down_pipe_kernel<RG, RPW, NV, 4>), grid, block, 0, st, d);
+    else
+        hipLaunchKernelGGL((lora_down_pipe_kernel<RG, RPW, NV, 8>), grid, block, 0, st, d);
+}
+
 // Ranks in passes of up to 64 (each pass reads X again); the side job rides
 // on the first pass.
 template <bool NV>
@@ -710,20 +733,19 @@ static pact_status launch_down_pipe(DownArgs d, hipStream_t st) {
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
         const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
         const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
-        const dim3 grid((unsigned)((d.M + (two ? 31 : 15)) / (two ? 32 : 16) +
-                                   (j0 == 0 ? side_blocks(d, 64 * kPipeWaves) : 0))),
-            block(64 * kPipeWaves);
+        const int groups = (d.M + (two ? 31 : 15)) / (two ? 32 : 16);
+        const int nw = pipe_waves(rg, two ? 2 : 1, groups);
+        const dim3 grid((unsigned)(groups + (j0 == 0 ? side_blocks(d, 64 * nw) : 0))), block(64 * nw);
         d.j0 = j0;
-#define PACT_DOWN_PIPE(RG)                                                                        \
-    if (two) hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 2, NV>), grid, block, 0, st, d);      \
-    else hipLaunchKernelGGL((lora_down_pipe_kernel<RG, 1, NV>), grid, block, 0, st, d);
-        switch (rg) {
-            case 1: PACT_DOWN_PIPE(1) break;
-            case 2: PACT_DOWN_PIPE(2) break;
-            case 3: PACT_DOWN_PIPE(3) break;
-            default: PACT_DOWN_PIPE(4) break;
+        switch (rg * 2 + (two ? 1 : 0)) {
+            case 2: launch_pipe_nw<1, 1, NV>(nw, grid, block, st, d); break;
+            case 4: launch_pipe_nw<2, 1, NV>(nw, grid, block, st, d); break;
+            case 5: launch_pipe_nw<2, 2, NV>(nw, grid, block, st, d); break;
+            case 6: launch_pipe_nw<3, 1, NV>(nw, grid, block, st, d); break;
+            case 7: launch_pipe_nw<3, 2, NV>(nw, grid, block, st, d); break;
+            case 8: launch_pipe_nw<4, 1, NV>(nw, grid, block, st, d); break;
+            default: launch_pipe_nw<4, 2, NV>(nw, grid, block, st, d); break;
         }
-#undef PACT_DOWN_PIPE
         PACT_TRY(launch_status());
     }
     return PACT_OK;
