@@ -604,8 +604,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: every step of the data flow is row-parallel, "
-              "and this build runs on a single MI355X (the sharding plan is in DESIGN.md).",
+        print("bench.py measures one GPU only (--gpus 1): every step of the data flow is row-parallel, so "
+              "tokens would shard across GPUs with no exchange in the forward and input-gradient passes, "
+              "but runs on more than one GPU are not supported here.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
