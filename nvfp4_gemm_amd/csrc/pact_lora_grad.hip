@@ -232,7 +232,7 @@ struct GradPlan {
 // CB = 256 columns for wide BF16 outputs with many tokens (the rank operand
 // is re-read once per column block), 128 otherwise; token splits for about 512
 // workgroups, down to one stage per workgroup and at most kMaxSplits (swept
-// on the box over the layer shapes: at M = 1024 the extra splits take a
+// on an MI355X over the layer shapes: at M = 1024 the extra splits take a
 // contraction from 13-19 to 9-15 us).
 static GradPlan grad_plan(int64_t M, int64_t C, bool nv) {
     const int cb = (!nv && C >= 4096 && M >= 4096) ? 256 : 128;
