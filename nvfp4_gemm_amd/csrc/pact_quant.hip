@@ -523,6 +523,31 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
     }
     const int64_t ngroups = (a.rows + RPW - 1) / RPW;
     const int rl = __builtin_amdgcn_readfirstlane(lrow);
+    // SiLU backward loops over row groups: the next group's operands are
+    // loaded while the current one is processed (up to 3 blocks per lane; 4
+    // would spill registers)
+    constexpr bool PF = MODE == MODE_SILU_BWD && BPL <= 3;
+    constexpr int BS = PF ? BPL : 1;
+    uint32_t pdw[BS][8], pc0[BS][2], ps0[BS], pc1[BS][2], ps1[BS];
+    float pd0 = 0.0f, pd1 = 0.0f;
+    auto fetch = [&](int64_t g) {
+        const int64_t prow = g * RPW + rl;
+        const bool pact = prow < a.rows;
+#pragma unroll
+        for (int i = 0; i < BS; ++i) {
+            const int b = lt + T * i;
+            if (pact && b < nb) {
+                load_block(a.dy + prow * a.lddy, 32u * (uint32_t)b, pdw[i]);
+                load_codes(a.in0, prow, cols, b, pc0[i][0], pc0[i][1], ps0[i]);
+                load_codes(a.in1, prow, cols, b, pc1[i][0], pc1[i][1], ps1[i]);
+            }
+        }
+        pd0 = pact ? a.in0.d[prow] : 0.0f;
+        pd1 = pact ? a.in1.d[prow] : 0.0f;
+    };
+    if constexpr (PF) {
+        if ((int64_t)blockIdx.x < ngroups) fetch(blockIdx.x);
+    }
     for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
         const int64_t row = grp * RPW + rl;
         const bool active = row < a.rows;
@@ -532,23 +557,43 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
         uint32_t c1[MODE == MODE_SILU_BWD ? BPL : 1][2], s1[MODE == MODE_SILU_BWD ? BPL : 1];
         uint32_t cw[MODE == MODE_RMS_BWD ? BPL : 1][8];
         bool valid[BPL];
+        float d0, d1 = 0.0f;
+        if constexpr (PF) {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int b = lt + T * i;
-            valid[i] = active && b < nb;
-            if (valid[i]) {
-                load_block(dyr, 32u * (uint32_t)b, dw[i]);
-                load_codes(a.in0, row, cols, b, c0[i][0], c0[i][1], s0[i]);
-                if constexpr (MODE == MODE_SILU_BWD) load_codes(a.in1, row, cols, b, c1[i][0], c1[i][1], s1[i]);
-                if constexpr (MODE == MODE_RMS_BWD) {
-                    if (a.C) load_block(a.C + row * a.ldc, 32u * (uint32_t)b, cw[i]);
+            for (int i = 0; i < BPL; ++i) {
+                valid[i] = active && lt + T * i < nb;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dw[i][j] = pdw[i][j];
+                c0[i][0] = pc0[i][0];
+                c0[i][1] = pc0[i][1];
+                s0[i] = ps0[i];
+                c1[i][0] = pc1[i][0];
+                c1[i][1] = pc1[i][1];
+                s1[i] = ps1[i];
+            }
+            d0 = pd0;
+            d1 = pd1;
+            if (grp + gridDim.x < ngroups) fetch(grp + gridDim.x);
+        } else {
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                const int b = lt + T * i;
+                valid[i] = active && b < nb;
+                if (valid[i]) {
+                    load_block(dyr, 32u * (uint32_t)b, dw[i]);
+                    load_codes(a.in0, row, cols, b, c0[i][0], c0[i][1], s0[i]);
+                    if constexpr (MODE == MODE_SILU_BWD) load_codes(a.in1, row, cols, b, c1[i][0], c1[i][1], s1[i]);
+                    if constexpr (MODE == MODE_RMS_BWD) {
+                        if (a.C) load_block(a.C + row * a.ldc, 32u * (uint32_t)b, cw[i]);
+                    }
                 }
             }
+            d0 = active ? a.in0.d[row] : 0.0f;
+            if constexpr (MODE == MODE_SILU_BWD) d1 = active ? a.in1.d[row] : 0.0f;
         }
-        const float d0 = active ? a.in0.d[row] : 0.0f;
+        (void)dyr;
 
         if constexpr (MODE == MODE_SILU_BWD) {
-            const float d1 = active ? a.in1.d[row] : 0.0f;
             float gmax[BPL], umax[BPL];
             float rg = 0.0f, ru = 0.0f;
             uint32_t gw[BPL][8], uw[BPL][8];  // dg, du as packed BF16

@@ -31,7 +31,7 @@ def _stash_gu(rng, rows, cols):
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 16), (5, 48), (7, 1040), (64, 4096), (33, 8192), (9, 8960),
-                                       (4, 9232), (3, 17408)])
+                                       (4, 9232), (3, 17408), (2, 25600)])
 def test_silu_mul_bwd_parity(rows, cols):
     rng = np.random.default_rng(rows * 7 + cols)
     gq, uq = _stash_gu(rng, rows, cols)
