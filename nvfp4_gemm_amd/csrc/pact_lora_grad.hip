@@ -237,7 +237,8 @@ struct GradPlan {
 static GradPlan grad_plan(int64_t M, int64_t C, bool nv) {
     const int cb = (!nv && C >= 4096 && M >= 4096) ? 256 : 128;
     const int64_t cblocks = (C + cb - 1) / cb;
-    int64_t ms = (512 + cblocks - 1) / cblocks;
+    const int64_t target = (nv && M >= 4096) ? 1024 : 512;
+    int64_t ms = (target + cblocks - 1) / cblocks;
     int64_t max_ms = (M + kGradMT - 1) / kGradMT;
     if (max_ms > kMaxSplits) max_ms = kMaxSplits;
     if (ms > max_ms) ms = max_ms;
