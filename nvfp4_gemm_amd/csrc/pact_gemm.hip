@@ -552,14 +552,16 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(DownArgs d) {
 // (p_sk == 1).  Its cost is the number of vector memory instructions in
 // flight per CU, and the rank operand P costs as many instructions as X (it is
 // read from L2 by every row group).  So: a wavefront takes RPW row groups and
-// uses every P fragment for all of them; NW = 8 or 16 wavefronts split K
+// uses every P fragment for all of them; NW = 4, 8 or 16 wavefronts split K
 // (enough wavefronts in flight even when the row groups are few); each
 // wavefront works through its K range in stages of 128 K with the loads of
 // the next stage issued before the MFMAs of the current one (branch-free: out
 // of range fragments read a clamped address and are zeroed).  Within a stage,
 // fragment c of lane group g covers 8 K at kpos(c, g): for BF16 rows a
 // row's 64 contiguous bytes per instruction; for NVFP4 rows the lane's 16
-// code bytes hold its 32 K (decoded to BF16 in registers).
+// code bytes hold its 32 K (decoded to BF16 in registers).  X is read with
+// ordinary (cached) loads: the two halves of a 128-byte line come from two
+// instructions, and nontemporal loads made the launch 3-10 % slower.
 template <bool NV>
 __device__ __forceinline__ int down_kpos(int c, int g) { return NV ? 32 * g + 8 * c : 32 * c + 8 * g; }
 
@@ -610,12 +612,12 @@ __global__ __launch_bounds__(64 * NW) void lora_down_pipe_kernel(DownArgs d) {
                 const uint8_t *sr = d.xs + (int64_t)row[q] * (d.Kl / 16) + kk / 16;
                 uint32_t s2;
                 if (k32) {
-                    xv[b][q][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cr));
+                    xv[b][q][0] = *reinterpret_cast<const u32x4 *>(cr);
                     s2 = *reinterpret_cast<const uint16_t *>(sr);
                 } else {  // rows of 16 K multiples: the second block may be past the row
                     const bool two = kk + 16 < d.Kl;
-                    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(cr));
-                    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr));
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(cr);
+                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr);
                     xv[b][q][0] = u32x4{lo.x, lo.y, hi.x, hi.y};
                     s2 = (uint32_t)sr[0] | ((uint32_t)sr[two ? 1 : 0] << 8);
                 }
@@ -627,8 +629,8 @@ __global__ __launch_bounds__(64 * NW) void lora_down_pipe_kernel(DownArgs d) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int k = kc + down_kpos<NV>(c, g);
-                    const u32x4 v = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(d.X + (int64_t)row[q] * d.ldx + (k < ke ? k : 0)));
+                    const u32x4 v =
+                        *reinterpret_cast<const u32x4 *>(d.X + (int64_t)row[q] * d.ldx + (k < ke ? k : 0));
                     xv[b][q][c] = k < ke ? v : u32x4{0u, 0u, 0u, 0u};
                 }
             }
