@@ -113,12 +113,12 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradArgs g) {
                 const uint8_t *sr = g.vs + (int64_t)m * (g.C / 16) + cl / 16;
                 uint32_t s2;
                 if (c32) {
-                    rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cr));
+                    rv[i] = *reinterpret_cast<const u32x4 *>(cr);
                     s2 = *reinterpret_cast<const uint16_t *>(sr);
                 } else {
                     const bool two = cl + 16 < g.C;
-                    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(cr));
-                    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr));
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(cr);
+                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(two ? cr + 8 : cr);
                     rv[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
                     s2 = (uint32_t)sr[0] | ((uint32_t)sr[two ? 1 : 0] << 8);
                 }
@@ -130,8 +130,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradArgs g) {
                 const int row = p / (CB / 8), col = c0 + 8 * (p % (CB / 8));
                 const int m = min(m0 + row, g.M - 1);
                 const bool ok = m0 + row < me && col < g.C;
-                const u32x4 v = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(g.V + (int64_t)m * g.ldv + (ok ? col : 0)));
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(g.V + (int64_t)m * g.ldv + (ok ? col : 0));
                 rv[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
             }
         }
