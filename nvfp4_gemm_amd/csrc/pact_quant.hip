@@ -183,15 +183,17 @@ __device__ __forceinline__ void unpack16(const uint32_t w[8], float v[16]) {
     }
 }
 
-// Streaming accesses: every input byte is read once and every output byte
-// written once, so loads and stores carry the nontemporal hint (no cache
-// allocation on the way through; measured 1.6x faster than cached loads on
-// 8192 x 8192 inputs).  gamma and the sigma32 table are reused and stay cached.
+// Input blocks are read with ordinary (cached) loads: inside a layer the
+// producer's output is often still in the Infinity Cache, and there cached
+// loads were faster (SiLU-multiply-quantize 8192 x 8192: 125-128 -> 107 us
+// per call within the layer step), although nontemporal loads had been 1.6x
+// faster on 8192 x 8192 inputs with the caches flushed.  Stores keep the
+// nontemporal hint.
 // base: row start (uniform across the wavefront); off: byte offset of the block.
 __device__ __forceinline__ void load_block(const uint16_t *base, uint32_t off, uint32_t w[8]) {
     const char *p = reinterpret_cast<const char *>(base) + off;
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 16);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
@@ -491,10 +493,10 @@ struct BwdArgs {
 
 __device__ __forceinline__ void load_codes(const CNV &q, int64_t row, int cols, int b, uint32_t &c0, uint32_t &c1,
                                            uint32_t &sb) {
-    const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q.codes + row * (cols / 2) + 8 * b));
+    const u32x2 c = *reinterpret_cast<const u32x2 *>(q.codes + row * (cols / 2) + 8 * b);
     c0 = c.x;
     c1 = c.y;
-    sb = __builtin_nontemporal_load(q.scales + row * (cols / 16) + b);
+    sb = q.scales[row * (cols / 16) + b];
 }
 
 __device__ __forceinline__ void pack16(const float v[16], uint32_t w[8]) {
