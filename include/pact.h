@@ -293,6 +293,23 @@ pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *s
 pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad, int32_t *kernel,
                                  int32_t *ks, int32_t *fused);
 
+/* Diagnostic: how the LoRA-down product T of the same GEMM call is computed
+ * (host only, no GPU work), given the full workspace.  Arguments as for
+ * pact_debug_gemm_plan, plus ngroups >= 1 projections of rank r each (a
+ * grouped forward; 1 for the plain entry points, and dgrad requires 1).
+ * *route: 1 = workgroups of the split-K main launch; 2 = the pipelined
+ * kernel on contiguous rank rows; 3 = a transpose of the input gradient's
+ * strided rank operand, then the pipelined kernel; 4 = the kernel that
+ * gathers strided rank rows.  Unless *route == 1, *npass passes over the
+ * ranks (64 per pass) are written to rg[i] (16-rank groups of the pass),
+ * rows_per_wave[i] (16-row groups per wavefront) and waves[i] (wavefronts
+ * per workgroup); each array must hold 4 entries.  PACT_ERR_INVALID_ARG for
+ * negative sizes, r < 1, ngroups outside 1..4, more than 256 padded ranks,
+ * or a null pointer. */
+pact_status pact_debug_lora_down_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t ngroups, int32_t dgrad,
+                                      int32_t *route, int32_t *npass, int32_t *rg, int32_t *rows_per_wave,
+                                      int32_t *waves);
+
 #ifdef __cplusplus
 }
 #endif

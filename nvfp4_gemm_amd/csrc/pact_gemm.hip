@@ -728,15 +728,28 @@ static void launch_pipe_nw(int nw, dim3 grid, dim3 block, hipStream_t st, const 
         hipLaunchKernelGGL((lora_down_pipe_kernel<RG, RPW, NV, 8>), grid, block, 0, st, d);
 }
 
+// One pass of the pipelined LoRA-down over ranks [j0, j0 + 16 rg): rank
+// groups, row groups of 16 per wavefront, wavefronts per workgroup and
+// workgroups with rows.
+struct PipePass {
+    int rg, rpw, nw, groups;
+};
+
+static PipePass pipe_pass(int64_t M, int rpad, int j0) {
+    const int rg = (rpad - j0) / 16 < 4 ? (rpad - j0) / 16 : 4;
+    const bool two = M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
+    const int groups = (int)((M + (two ? 31 : 15)) / (two ? 32 : 16));
+    return {rg, two ? 2 : 1, pipe_waves(rg, two ? 2 : 1, groups), groups};
+}
+
 // Ranks in passes of up to 64 (each pass reads X again); the side job rides
 // on the first pass.
 template <bool NV>
 static pact_status launch_down_pipe(DownArgs d, hipStream_t st) {
     for (int j0 = 0; j0 < d.rpad; j0 += 64) {
-        const int rg = (d.rpad - j0) / 16 < 4 ? (d.rpad - j0) / 16 : 4;
-        const bool two = d.M >= 4096 && rg >= 2;  // two row groups per wavefront once rows are plentiful
-        const int groups = (d.M + (two ? 31 : 15)) / (two ? 32 : 16);
-        const int nw = pipe_waves(rg, two ? 2 : 1, groups);
+        const PipePass pp = pipe_pass(d.M, d.rpad, j0);
+        const int rg = pp.rg, nw = pp.nw, groups = pp.groups;
+        const bool two = pp.rpw == 2;
         const dim3 grid((unsigned)(groups + (j0 == 0 ? side_blocks(d, 64 * nw) : 0))), block(64 * nw);
         d.j0 = j0;
         switch (rg * 2 + (two ? 1 : 0)) {
@@ -1840,6 +1853,38 @@ extern "C" pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int
     *kernel = plan.kernel;
     *ks = plan.ks;
     if (fused) *fused = plan.fuse ? 1 : 0;
+    return PACT_OK;
+}
+
+extern "C" pact_status pact_debug_lora_down_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t ngroups,
+                                                 int32_t dgrad, int32_t *route, int32_t *npass, int32_t *rg,
+                                                 int32_t *rows_per_wave, int32_t *waves) {
+    if (M < 0 || N < 0 || K < 0 || r < 1 || ngroups < 1 || ngroups > kMaxGroups || (dgrad && ngroups != 1) ||
+        ngroups * round_up(r, 16) > 256 || !route || !npass || !rg || !rows_per_wave || !waves)
+        return PACT_ERR_INVALID_ARG;
+    const int rpad = ngroups * (int)round_up(r, 16);
+    const GemmPlan plan = plan_gemm(M, N, K, device_cus(), DownPlan{K, dgrad != 0, rpad});
+    *npass = 0;
+    if (plan.fuse && plan.ks > 1 && rpad <= 64) {
+        *route = 1;
+        return PACT_OK;
+    }
+    // the input gradient's rank operand B [N][r] has strided rank rows (unless r == 1)
+    const bool strided = dgrad && r > 1;
+    *route = dgrad && M >= 4096 ? 3 : (strided ? 4 : 2);
+    for (int j0 = 0; j0 < rpad; j0 += 64) {
+        const int i = (*npass)++;
+        if (*route == 4) {
+            rg[i] = (rpad - j0) / 16 < 4 ? (rpad - j0) / 16 : 4;
+            rows_per_wave[i] = 1;
+            waves[i] = kDownWaves;
+        } else {
+            const PipePass pp = pipe_pass(M, rpad, j0);
+            rg[i] = pp.rg;
+            rows_per_wave[i] = pp.rpw;
+            waves[i] = pp.nw;
+        }
+    }
     return PACT_OK;
 }
 

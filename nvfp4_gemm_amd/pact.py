@@ -40,7 +40,8 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_gemm_workspace", "pact_gemm_nvfp4_fwd", "pact_gemm_nvfp4_dgrad",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
-           "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped"]
+           "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
+           "pact_debug_lora_down_plan"]
 
 
 class PactError(RuntimeError):
@@ -100,6 +101,10 @@ def lib():
         L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
+        I32P = ctypes.POINTER(ctypes.c_int32)
+        L.pact_debug_lora_down_plan.restype = st
+        L.pact_debug_lora_down_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                I32P, I32P, I32P, I32P, I32P]
         _lib = L
     return _lib
 
@@ -413,3 +418,20 @@ def pact_debug_gemm_plan(M: int, N: int, K: int, r: int = 0, dgrad: bool = False
     _check(lib().pact_debug_gemm_plan(M, N, K, r, 1 if dgrad else 0, ctypes.byref(k), ctypes.byref(ks),
                                       ctypes.byref(f)), "pact_debug_gemm_plan")
     return k.value, ks.value, bool(f.value)
+
+
+LORA_DOWN_ROUTES = {1: "fused into the split-K launch", 2: "pipelined", 3: "transpose, then pipelined",
+                    4: "strided gather"}
+
+
+def pact_debug_lora_down_plan(M: int, N: int, K: int, r: int, ngroups: int = 1,
+                              dgrad: bool = False) -> tuple[int, list[tuple[int, int, int]]]:
+    """(route, passes) of the LoRA-down product of the GEMM call with output
+    [M][N] over K, rank r per projection and ngroups projections (host only):
+    route as in LORA_DOWN_ROUTES; passes = [(rank groups, row groups per
+    wavefront, wavefronts per workgroup), ...], empty when fused."""
+    route, npass = ctypes.c_int32(), ctypes.c_int32()
+    rg, rpw, nw = (ctypes.c_int32 * 4)(), (ctypes.c_int32 * 4)(), (ctypes.c_int32 * 4)()
+    _check(lib().pact_debug_lora_down_plan(M, N, K, r, ngroups, 1 if dgrad else 0, ctypes.byref(route),
+                                           ctypes.byref(npass), rg, rpw, nw), "pact_debug_lora_down_plan")
+    return route.value, [(rg[i], rpw[i], nw[i]) for i in range(npass.value)]

@@ -70,3 +70,26 @@ def check_gemm_tolerance(got_bits: np.ndarray, ref_bits: np.ndarray, what=""):
         rel = np.linalg.norm(g - r) / nr
         assert rel <= 4e-3, f"{what}: relative Frobenius error {rel}"
     return float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
+
+
+
+def check_lora_grads(gdA, gdB, dA, dB, what=""):
+    """GPU LoRA gradients (FP32) against the oracle's (float64).  Both share
+    the rank index j: dA [r,K] row j and dB [N,r] column j are the products of
+    one rank intermediate (T'[:, j], T^[:, j]) with the tokens, so an entry of
+    T^ or T' that rounds to the neighbouring BF16 value on one side moves that
+    whole row or column together.  Bound, in the GEMM's form with "row" read
+    as "the entries of one rank": per element |d| <= 2 ulp_bf16(|ref|) +
+    1e-3 max_j|ref|, and a relative Frobenius error <= 4e-3."""
+    for got, ref, axis, name in ((gdA, dA, 1, "dA"), (gdB, dB, 0, "dB")):
+        g = got.cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+        rank_max = np.max(np.abs(ref), axis=axis, keepdims=True) if ref.size else ref
+        bound = 2 * ulp_bf16(ref) + 1e-3 * rank_max
+        err = np.abs(g - ref)
+        bad = err > bound
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"{what} {name}: {bad.sum()} elements out of tolerance, first {i}: got {g[i]} "
+                                 f"ref {ref[i]} bound {bound[i]}")
+        nr = np.linalg.norm(ref)
+        assert np.linalg.norm(g - ref) <= 4e-3 * nr + 1e-30, f"{what} {name}: relative Frobenius error"

@@ -157,6 +157,37 @@ def test_gemm_plan_lora_down_placement(L):
     assert fu.value == 0 or ks.value > 2
 
 
+def test_lora_down_plan_host_logic(L):
+    """The LoRA-down diagnostic agrees with the GEMM plan (route 1 exactly
+    when the plan fuses it into the split-K launch), takes one pass per 64
+    padded ranks, and rejects invalid arguments without touching a device."""
+    i32 = ctypes.c_int32
+    route, npass = i32(), i32()
+    rg, rpw, nw = (i32 * 4)(), (i32 * 4)(), (i32 * 4)()
+    call = lambda *a: L.pact_debug_lora_down_plan(*a, ctypes.byref(route), ctypes.byref(npass), rg, rpw, nw)
+    assert call(-1, 8, 8, 16, 1, 0) == 1
+    assert call(8, 8, 8, 0, 1, 0) == 1
+    assert call(8, 8, 8, 16, 0, 0) == 1
+    assert call(8, 8, 8, 16, 5, 0) == 1                 # more groups than a grouped GEMM takes
+    assert call(8, 8, 8, 16, 2, 1) == 1                 # the input gradient has one projection
+    assert call(8, 8, 8, 96, 3, 0) == 1                 # 288 padded ranks
+    assert L.pact_debug_lora_down_plan(8, 8, 8, 16, 1, 0, None, ctypes.byref(npass), rg, rpw, nw) == 1
+    k, ks, fu = i32(), i32(), i32()
+    for M, N, K, r, g, dg in [(1024, 2048, 8192, 16, 1, 0), (4096, 1536, 8960, 16, 1, 0), (1024, 512, 2048, 16, 1, 1),
+                              (8192, 5120, 3072, 32, 3, 0), (8192, 3072, 8192, 32, 1, 1), (256, 1024, 512, 8, 1, 0)]:
+        assert call(M, N, K, r, g, dg) == 0
+        assert L.pact_debug_gemm_plan(M, N, K, r * g if g > 1 else r, dg, ctypes.byref(k), ctypes.byref(ks),
+                                      ctypes.byref(fu)) == 0
+        assert (route.value == 1) == (fu.value == 1 and ks.value > 1)
+        if route.value != 1:
+            rpad = g * ((r + 15) // 16 * 16)
+            assert npass.value == (rpad + 63) // 64
+            assert sum(rg[i] for i in range(npass.value)) * 16 == rpad
+            assert all(rpw[i] == (2 if M >= 4096 and rg[i] >= 2 and route.value != 4 else 1)
+                       for i in range(npass.value))
+            assert route.value == (3 if dg and M >= 4096 else (4 if dg else 2))
+
+
 def test_backward_validation(L):
     """Argument checks of the backward entry points (host only, nothing is
     launched on an error)."""

@@ -36,8 +36,8 @@ def _lora(li, r):
     return li.A[:r], li.B[:, :r], pb.LoRA(G.dev_bf16(li.A[:r]), G.dev_bf16(li.B[:, :r]), li.s)
 
 
-def _run_pair(M, N, K, r, seed, with_c, act="t4", rows=None):
-    li = synth.single_linear_inputs(M=M, N=N, K=K, r=max(r, 1), seed=seed, act=act, outliers=True)
+def _run_pair(M, N, K, r, seed, with_c, act="t4", rows=None, s=2.0):
+    li = synth.single_linear_inputs(M=M, N=N, K=K, r=max(r, 1), s=s, seed=seed, act=act, outliers=True)
     A, B, lora = _lora(li, r)
     rng = np.random.default_rng(seed + 1)
     C = synth.normal_bf16(rng, (M, N), 0.5) if with_c else None

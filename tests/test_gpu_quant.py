@@ -9,7 +9,9 @@ import torch
 import oracle
 from nvfp4_gemm_amd import pact as pb
 from nvfp4_gemm_amd import synth
+from tests import _exact as ex
 from tests import _gpu as G
+from tests.test_oracle_quant import representable_row
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +27,60 @@ def _edge_rows(cols, rng):
     t[::7] = -1e-30
     rows.append(t)
     return synth.to_bf16_bits(np.stack(rows))
+
+
+def _tie_rows(cols, rng):
+    """Rows with closed-form codes (representable_row): row scale 2^k, every
+    element an E2M1 value times its block's E4M3 scale, and with ties=True
+    elements placed exactly on the E2M1 rounding midpoints 0.25 ... 5 (times
+    the block scale), which round to the even code."""
+    xs, codes, scales, ks = [], [], [], []
+    for k in (-24, -3, 0, 7):
+        for ties in (False, True, True):
+            x, c, sc = representable_row(rng, cols // 16, k, ties)
+            xs.append(x), codes.append(c), scales.append(sc), ks.append(k)
+    return np.stack(xs), np.stack(codes), np.stack(scales), np.array(ks)
+
+
+def _saturating_rows(cols, rng, n=6):
+    """Rows whose blocks span 20 binades below the row maximum: many block
+    scales fall in E4M3's subnormal range (or round down), so the block's
+    largest elements lie above 6 times the block scale and saturate to 6."""
+    nb = cols // 16
+    x = rng.standard_normal((n, cols))
+    x *= np.repeat(np.exp2(-rng.uniform(0, 20, (n, nb))), 16, axis=1)
+    return synth.to_bf16_bits(x)
+
+
+def _count_saturated(xb, q):
+    """Elements with |x| > 6 S_b (S_b = decoded block scale times row scale)."""
+    sc = np.array([oracle.e4m3_value(i) for i in range(256)], np.float64)
+    S = sc[q.scales].repeat(16, axis=1) * q.d.astype(np.float64)[:, None]
+    xf = np.abs(synth.bf16_bits_to_f32(xb).astype(np.float64))
+    return int(np.sum((S > 0) & (xf > 6 * S)))
+
+
+@pytest.mark.parametrize("cols", [16, 512, 3072, 8960])
+def test_quantize_ties_and_saturation(cols):
+    """E2M1 ties to even and saturation at 6 through the GPU's converter:
+    closed-form codes on tie-crafted representable rows, the oracle's codes on
+    rows that saturate (the test checks that they do)."""
+    rng = np.random.default_rng(cols + 11)
+    X, C, S, ks = _tie_rows(cols, rng)
+    xb = synth.to_bf16_bits(X)
+    assert np.array_equal(synth.bf16_bits_to_f32(xb).astype(np.float64), X)  # exact in BF16
+    sat = _saturating_rows(cols, rng)
+    allx = np.concatenate([xb, sat])
+    want = oracle.quantize_bf16(allx)
+    assert _count_saturated(sat, oracle.quantize_bf16(sat)) > 0
+    got = pb.pact_quantize_nvfp4(G.dev_bf16(allx))
+    torch.cuda.synchronize()
+    G.assert_nvfp4_equal(got, want, f"ties/saturation {cols}")
+    gh = G.host_nvfp4(got)
+    n = X.shape[0]
+    np.testing.assert_array_equal(ex.unpack_codes(gh.codes[:n]), C)
+    np.testing.assert_array_equal(gh.scales[:n], S)
+    np.testing.assert_array_equal(gh.d[:n], np.exp2(ks).astype(np.float32))
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (5, 512), (7, 1024), (33, 3072),
@@ -70,8 +126,11 @@ def test_rmsnorm_parity(rows, cols, eps):
 @pytest.mark.parametrize("rows,cols", [(6, 256), (9, 8192), (5, 8960), (4, 9232), (3, 1536), (70, 16)])
 def test_silu_parity(rows, cols):
     rng = np.random.default_rng(rows + 3 * cols)
-    g = np.concatenate([synth.student_t_bf16(rng, (rows, cols), 4.0, 0.5), _edge_rows(cols, rng)])
-    u = np.concatenate([synth.student_t_bf16(rng, (rows, cols), 4.0, 0.5), _edge_rows(cols, rng)[::-1]])
+    ties = synth.to_bf16_bits(_tie_rows(cols, rng)[0][:4])
+    sat = _saturating_rows(cols, rng, n=4)
+    g = np.concatenate([synth.student_t_bf16(rng, (rows, cols), 4.0, 0.5), _edge_rows(cols, rng), ties, sat])
+    u = np.concatenate([synth.student_t_bf16(rng, (rows, cols), 4.0, 0.5), _edge_rows(cols, rng)[::-1], sat,
+                        ties])
     h, hq, gq, uq = oracle.silu_mul_quant(g, u)
     gh, ghq, ggq, guq = pb.pact_silu_mul_quant_nvfp4(G.dev_bf16(g), G.dev_bf16(u))
     _, ghq2, n1, n2 = pb.pact_silu_mul_quant_nvfp4(G.dev_bf16(g), G.dev_bf16(u), want_h=False,
