@@ -271,6 +271,26 @@ pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int6
 pact_status pact_adamw_step(float *p, float *m, float *v, const float *g, uint16_t *w, int64_t n, float lr,
                             float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream);
 
+/* Forward GEMM for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation):
+ * pact_gemm_nvfp4_fwd with the same arguments and results, but its workspace
+ * is a library-owned device array of PACT_NOALLOC_SCRATCH_BYTES bytes, one
+ * per GPU, held until the process ends; the call itself allocates nothing.
+ * The LoRA-down product [M][round_up(r, 16)] BF16 must fit in that array
+ * (else PACT_ERR_WORKSPACE, nothing launched); when the K-split partials do
+ * not fit as well, the GEMM runs in one pass over K (same tolerance).  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams or threads without ordering between them) race and
+ * give undefined results.  Nothing in the array needs clearing between calls:
+ * every byte a call reads was written earlier in the same call.  The first
+ * call on each device looks the array's address up with that device current;
+ * PACT_ERR_HIP when the lookup fails. */
+#define PACT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+size_t pact_noalloc_scratch_bytes(void);
+pact_status pact_gemm_nvfp4_fwd_noalloc(const pact_nvfp4 *Xq, const uint16_t *X, int64_t ld_x,
+                                        const pact_nvfp4 *W_fwd, const pact_lora *lora, const uint16_t *C,
+                                        uint16_t *Y, int64_t ld_y, void *stream);
+
 /* Diagnostic: out[i] = sigma32(g[i]) (the binary32 sigmoid-times-input the
  * SiLU kernel uses) for n BF16 inputs g, so that it can be checked against a
  * reference over all 65536 BF16 values.  Device pointers; stream-ordered. */

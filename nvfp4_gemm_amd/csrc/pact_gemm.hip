@@ -29,6 +29,7 @@
 // LoRA-up product T Q^T is accumulated by BF16 MFMAs into the row-scaled
 // accumulators in the epilogue.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1955,4 +1956,56 @@ extern "C" pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16
     // T' = dY B: P(j, n) = B[n r + j];  L' = T' A: Q(k, j) = A[j K + k]
     return gemm_common(dYq, W_bwd, dY, ld_dy, N, lora, lora ? lora->B : nullptr, 1, r,
                        lora ? lora->A : nullptr, 1, K, C, dX, ld_dx, ws, ws_bytes, stream);
+}
+
+// ---- forward GEMM with a library-owned workspace (no allocation) ----------
+// For callers that cannot allocate device memory (code under stream capture,
+// tight serving loops, harnesses that forbid allocation): the workspace of
+// pact_gemm_nvfp4_fwd lives in this file-scope device array, one copy per
+// GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is looked up once per
+// device and only that address is handed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = PACT_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current).
+pact_status scratch_on_current_device(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PACT_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return PACT_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PACT_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PACT_OK;
+}
+
+}  // namespace
+
+extern "C" size_t pact_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" pact_status pact_gemm_nvfp4_fwd_noalloc(const pact_nvfp4 *Xq, const uint16_t *X, int64_t ld_x,
+                                                   const pact_nvfp4 *W_fwd, const pact_lora *lora,
+                                                   const uint16_t *C, uint16_t *Y, int64_t ld_y, void *stream) {
+    if (!Xq || !W_fwd) return PACT_ERR_INVALID_ARG;
+    const int r = lora ? lora->r : 0;
+    // the LoRA-down product must fit; split-K partials and rank-operand
+    // copies that do not fit are left out (one pass over K instead)
+    if (r > 0 && (r > 256 || Xq->rows < 0 || lora_ws_bytes(Xq->rows, r) > kScratchBytes)) return PACT_ERR_WORKSPACE;
+    void *ws = nullptr;
+    PACT_TRY(scratch_on_current_device(&ws));
+    const int64_t K = Xq->cols;
+    return gemm_common(Xq, W_fwd, X, ld_x, K, lora, lora ? lora->A : nullptr, K, 1, lora ? lora->B : nullptr, r, 1,
+                       C, Y, ld_y, ws, kScratchBytes, stream);
 }

@@ -41,7 +41,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
            "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
-           "pact_debug_lora_down_plan"]
+           "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc"]
 
 
 class PactError(RuntimeError):
@@ -101,6 +101,10 @@ def lib():
         L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
+        L.pact_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        L.pact_noalloc_scratch_bytes.argtypes = []
+        L.pact_gemm_nvfp4_fwd_noalloc.restype = st
+        L.pact_gemm_nvfp4_fwd_noalloc.argtypes = [NV, P, I64, NV, LO, P, P, I64, P]
         I32P = ctypes.POINTER(ctypes.c_int32)
         L.pact_debug_lora_down_plan.restype = st
         L.pact_debug_lora_down_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -289,6 +293,26 @@ def pact_gemm_nvfp4_fwd(Xq: NVFP4Tensor, W_fwd: NVFP4Tensor, X=None, lora: LoRA 
     """Y = bf16(d_x d_w Xq.W_fwd^T + s bf16(X A^T) B^T (+ C))."""
     return _gemm(lib().pact_gemm_nvfp4_fwd, "pact_gemm_nvfp4_fwd", Xq, X, W_fwd, lora, C, Y, ws,
                  stream)
+
+
+def pact_noalloc_scratch_bytes() -> int:
+    return int(lib().pact_noalloc_scratch_bytes())
+
+
+def pact_gemm_nvfp4_fwd_noalloc(Xq: NVFP4Tensor, W_fwd: NVFP4Tensor, X=None, lora: LoRA | None = None,
+                                C=None, Y=None, stream=None):
+    """pact_gemm_nvfp4_fwd with the library's own per-GPU workspace (the call
+    allocates nothing; Y must be given for that)."""
+    M, N = Xq.rows, W_fwd.rows
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=Xq.codes.device)
+    da, db = Xq.desc(), W_fwd.desc()
+    dl = lora.desc() if lora is not None else None
+    _check(lib().pact_gemm_nvfp4_fwd_noalloc(ctypes.byref(da), _ptr(X), _ld(X) if X is not None else 0,
+                                             ctypes.byref(db), ctypes.byref(dl) if dl is not None else None,
+                                             _ptr(C), _ptr(Y), _ld(Y), _stream(stream)),
+           "pact_gemm_nvfp4_fwd_noalloc")
+    return Y
 
 
 def pact_gemm_nvfp4_fwd_grouped(Xq: NVFP4Tensor, W_cat: NVFP4Tensor, group_rows, X=None, loras=None, Y=None,

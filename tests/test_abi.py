@@ -188,6 +188,19 @@ def test_lora_down_plan_host_logic(L):
             assert route.value == (3 if dg and M >= 4096 else (4 if dg else 2))
 
 
+def test_noalloc_gemm_rejects_oversized_lora_product(L):
+    """The no-allocation forward GEMM refuses, before any device work, a
+    LoRA-down product larger than its fixed per-GPU array (600000 rows x 32
+    ranks of BF16 = 38.4 MB > 32 MiB), and null operands."""
+    assert L.pact_noalloc_scratch_bytes() == 32 << 20
+    x = pb.pact_nvfp4(16, 16, 16, 600000, 256)
+    w = pb.pact_nvfp4(16, 16, 16, 64, 256)
+    lo = pb.pact_lora(16, 16, 32, 2.0)
+    assert L.pact_gemm_nvfp4_fwd_noalloc(ctypes.byref(x), 16, 256, ctypes.byref(w), ctypes.byref(lo), None, 16, 64,
+                                         None) == 4  # PACT_ERR_WORKSPACE
+    assert L.pact_gemm_nvfp4_fwd_noalloc(None, 16, 256, ctypes.byref(w), None, None, 16, 64, None) == 1
+
+
 def test_backward_validation(L):
     """Argument checks of the backward entry points (host only, nothing is
     launched on an error)."""
