@@ -75,10 +75,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="llama1b_layer", choices=CONFIGS)
+    ap.add_argument("--config", default="llama3b_stack28", choices=CONFIGS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="tokens in the oracle sample (0: the whole batch, at most 1024)")
+                    help="tokens in the oracle sample (0: 1024, or 512 for the 3B-shaped layers)")
     ap.add_argument("--lora-grads", action="store_true",
                     help="add the LoRA weight gradients (dA, dB of every projection, from the NVFP4 stash) "
                          "to each layer's backward and one fused AdamW step over all adapters; timed as their "
@@ -736,7 +736,10 @@ def main():
         if args.config == "single_linear":
             out["cpu_baseline"] = cpu_baseline_linear(work)
         else:
-            n = args.cpu_sample_tokens or min(work.M, 1024)
+            # about 10-30 s of oracle work on the host: 1024 tokens of the
+            # smaller layers, 512 of the 3B-shaped ones (403 MFLOP per token)
+            per_token = 2 * sum(2 * n_ * k_ for n_, k_ in work.S.projections().values())
+            n = args.cpu_sample_tokens or min(work.M, 1024 if per_token < 3e8 else 512)
             out["cpu_baseline"] = cpu_baseline_layer(work.S, work.li0, n)
     print(json.dumps(out), flush=True)
 
