@@ -69,6 +69,19 @@ struct GemmArgs {
     DownArgs down;  // ks > 1 and down.X: the LoRA-down runs as workgroups blockIdx.y == 0
 };
 
+// The GemmArgs argument of a kernel, read in place from the kernel-argument
+// segment, where it is the first (and only) explicit argument, at offset 0.
+// Referring to the by-value parameter itself lets the compiler copy the
+// struct into private memory when it cannot resolve every use (dynamically
+// indexed members), and the values loaded back from there count as
+// divergent: buffer descriptors end up in VGPRs and every buffer access
+// becomes a read-first-lane loop.  Read through this reference, every field
+// is a scalar load.
+__device__ __forceinline__ const GemmArgs &kernel_gemm_args() {
+    return *(const GemmArgs *)(const __attribute__((address_space(4))) GemmArgs *)
+        __builtin_amdgcn_kernarg_segment_ptr();
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Word 3 of the buffer resource descriptors (raw buffer access).
@@ -140,10 +153,27 @@ __device__ __forceinline__ EpiLora epi_lora(const GemmArgs &p, int mb, int nb, i
 }
 
 struct EpiIn {
-    float dx[16];    // d_a of the lane's 16 rows
     float dw;        // d_b of the lane's column
     u32x4 t[2], q[2];  // LoRA operands, ranks [0, 32) (prefetched when rpad <= 32)
 };
+
+// d_a of the lane's 16 rows of the fragments whose rows start at mb (shared
+// by the horizontally adjacent fragments of an epilogue group).
+__device__ __forceinline__ void epi_load_dx(const GemmArgs &p, int mb, int lane, float (&dx)[16]) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        const int m = mb + 8 * e4 + 4 * h;
+        if (m + 3 < p.M) {
+            const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dx[4 * e4 + q] = v[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dx[4 * e4 + q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
+        }
+    }
+}
 
 __device__ __forceinline__ bool epi_lora_prefetch(const GemmArgs &p) {
     return p.T && p.rpad <= 32 && p.q_sj == 1 && (p.r & 7) == 0;
@@ -155,18 +185,6 @@ __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int 
     const int h = lane >> 5, lr = lane & 31;
     const int n = nb + lr;
     in.dw = n < p.N ? p.b_d[n] : 0.0f;
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-        const int m = mb + 8 * e4 + 4 * h;
-        if (m + 3 < p.M) {
-            const float4_t v = *reinterpret_cast<const float4_t *>(p.a_d + m);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) in.dx[4 * e4 + q] = v[q];
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) in.dx[4 * e4 + q] = m + q < p.M ? p.a_d[m + q] : 0.0f;
-        }
-    }
     if (epi_lora_prefetch(p)) {
         const int mr = min(mb + lr, p.M - 1);
         const int nr = min(n, p.N - 1);
@@ -197,22 +215,23 @@ __device__ __forceinline__ void epi_load(const GemmArgs &p, int mb, int nb, int 
     }
 }
 
-// Row scales and LoRA term, in place, in the accumulator layout.
+// Row scales and LoRA term, in place, in the accumulator layout:
+// y = fl32(fl32(acc d_a) d_b), then + L with L = T_s . Q^T accumulated by
+// BF16 MFMAs (lane = column).  L is accumulated from zero in registers of
+// its own: accumulating it into the GEMM's accumulator ties the MFMA to
+// those registers and makes the compiler spill around it.
 __device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int mb, int nb, int lane,
-                                           const EpiIn &in) {
-    const int h = lane >> 5, lr = lane & 31;
-    const int n = nb + lr;
+                                           const EpiIn &in, const float (&dx)[16]) {
+    const int h = lane >> 5;
+    float16_t lo;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const float y = a[e] * in.dx[e];
-        a[e] = y * in.dw;
-    }
+    for (int e = 0; e < 16; ++e) lo[e] = 0.0f;
     if (epi_lora_prefetch(p)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             if (16 * i < p.rpad)
-                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, in.t[i]),
-                                                            __builtin_bit_cast(bf16x8_t, in.q[i]), a, 0, 0, 0);
+                lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, in.t[i]),
+                                                             __builtin_bit_cast(bf16x8_t, in.q[i]), lo, 0, 0, 0);
     } else if (p.T) {
         const EpiLora L = epi_lora(p, mb, nb, lane);
         for (int kk = 0; kk < p.rpad; kk += 16) {
@@ -227,15 +246,24 @@ __device__ __forceinline__ void epi_finish(const GemmArgs &p, float16_t &a, int 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int ja = j0 + 2 * e, jb = ja + 1;
-                    const uint32_t lo = ja < p.r ? L.Q[(int64_t)ja * p.q_sj] : 0u;
-                    const uint32_t hi = jb < p.r ? L.Q[(int64_t)jb * p.q_sj] : 0u;
-                    w[e] = lo | (hi << 16);
+                    const uint32_t lw = ja < p.r ? L.Q[(int64_t)ja * p.q_sj] : 0u;
+                    const uint32_t hw = jb < p.r ? L.Q[(int64_t)jb * p.q_sj] : 0u;
+                    w[e] = lw | (hw << 16);
                 }
                 vb = u32x4{w[0], w[1], w[2], w[3]};
             }
-            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
-                                                        __builtin_bit_cast(bf16x8_t, vb), a, 0, 0, 0);
+            lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                         __builtin_bit_cast(bf16x8_t, vb), lo, 0, 0, 0);
         }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float y = a[e] * dx[e];
+        a[e] = y * in.dw;
+    }
+    if (p.T) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a[e] = a[e] + lo[e];
     }
 }
 
@@ -391,6 +419,8 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
     static_for<F / G>([&](auto gc) {
         constexpr int g = decltype(gc)::value * G;
         EpiIn in[G];
+        float dx[16];
+        epi_load_dx(p, mb[g], lane, dx);
         static_for<G>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             epi_load(p, mb[g + i], nb[g + i], lane, in[i]);
@@ -398,7 +428,7 @@ __device__ __forceinline__ void epi_frags(const GemmArgs &p, int lane, AccFn &&a
         static_for<G>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             float16_t &a = accf(std::integral_constant<int, g + i>{});
-            epi_finish(p, a, mb[g + i], nb[g + i], lane, in[i]);
+            epi_finish(p, a, mb[g + i], nb[g + i], lane, in[i], dx);
             epi_to_tile<G>(tile, a, i, lane);
         });
         // LDS operations of one wavefront complete in order; the wait keeps
@@ -881,7 +911,9 @@ struct GemmShape {
 };
 
 template <int WM, int WN, int WK, bool KFULL, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p_arg) {
+    const GemmArgs &p = kernel_gemm_args();
+    (void)p_arg;
     using SH = GemmShape<WM, WN, WK>;
     static_assert(SH::LDS_BYTES >= 4 * 4 * epi_tile_floats<4>(), "LDS holds the epilogue tiles");
     static_assert(SH::LDS_BYTES >= 4 * down_red_floats<4, 4>(), "LDS holds the fused LoRA-down buffer");
@@ -1232,7 +1264,9 @@ __device__ __forceinline__ void wait_vmcnt_lds_barrier() {
 }
 
 template <bool SPLIT>
-__global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
+__global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p_arg) {
+    const GemmArgs &p = kernel_gemm_args();
+    (void)p_arg;
     using SH = Gemm8Shape;
     static_assert(SH::LDS_BYTES >= 8 * 4 * epi_tile_floats<2>(), "LDS holds the epilogue tiles");
     static_assert(SH::LDS_BYTES >= 4 * down_red_floats<4, 8>(), "LDS holds the fused LoRA-down buffer");
@@ -1426,7 +1460,9 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
 // run) and runs the epilogue on the sums.  A fragment past the output (FN not
 // a multiple of G) reads nothing and stores nothing.
 template <int G>
-__global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p_arg) {
+    const GemmArgs &p = kernel_gemm_args();
+    (void)p_arg;
     __shared__ __attribute__((aligned(16))) float tiles[4][epi_tile_floats<G>()];
     const int FM = (p.M + 31) >> 5, FN = (p.N + 31) >> 5, FNG = (FN + G - 1) / G;
     const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -1443,6 +1479,8 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
     // the epilogue's operands (row and column scales, LoRA rows, C) are
     // loaded first, so their latency overlaps that of the partials
     EpiIn in[G];
+    float dx[16];
+    epi_load_dx(p, mbs[0], lane, dx);
 #pragma unroll
     for (int i = 0; i < G; ++i) epi_load(p, mbs[i], nbs[i], lane, in[i]);
     u32x4 cv[2 * G];
@@ -1473,7 +1511,7 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p) {
     float *tile = tiles[threadIdx.x >> 6];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        epi_finish(p, acc[i], mbs[i], nbs[i], lane, in[i]);
+        epi_finish(p, acc[i], mbs[i], nbs[i], lane, in[i], dx);
         epi_to_tile<G>(tile, acc[i], i, lane);
     }
     // LDS operations of one wavefront complete in order; the wait keeps the
