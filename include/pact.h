@@ -313,6 +313,15 @@ pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *s
 pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad, int32_t *kernel,
                                  int32_t *ks, int32_t *fused);
 
+/* Diagnostic: the column split of the same launch plan (host only): when
+ * *n1 > 0, output columns [0, *n1) run as one launch of the kernel that
+ * pact_debug_gemm_plan reports and columns [*n1, N) as a second launch of
+ * kernel *kernel2 (numbered as there), so that whole rounds of workgroups
+ * fill the CUs; *n1 == 0: one launch.  PACT_ERR_INVALID_ARG as for
+ * pact_debug_gemm_plan. */
+pact_status pact_debug_gemm_plan_columns(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad, int32_t *n1,
+                                         int32_t *kernel2);
+
 /* Diagnostic: how the LoRA-down product T of the same GEMM call is computed
  * (host only, no GPU work), given the full workspace.  Arguments as for
  * pact_debug_gemm_plan, plus ngroups >= 1 projections of rank r each (a

@@ -1524,10 +1524,17 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(GemmArgs p_arg) {
 // Kernel: 0 = the 256 x 256 kernel (K % 64 == 0), 1..4 = the main kernel with
 // wavefronts (WM, WN, WK) = (2,2,1), (2,1,2), (1,2,2), (1,1,4).  ks: K ranges
 // split across workgroups, summed by the split-K epilogue kernel.
+// Column split (n1 > 0, ks == 1): output columns [0, n1) run as one launch of
+// `kernel`, chosen so that its 256 x 256 tiles fill whole rounds of the CUs,
+// and columns [n1, N) as a second launch of `kernel2` with smaller tiles, so
+// the last, partly filled round of one launch becomes a full round of smaller
+// tiles.
 struct GemmPlan {
     int kernel;
     int ks;
-    bool fuse;  // the LoRA-down runs as a row of workgroups of the split-K launch
+    bool fuse;    // the LoRA-down runs as a row of workgroups of the split-K launch
+    int n1 = 0;   // column split: columns of the first launch (multiple of 256), 0: none
+    int kernel2 = 0;
 };
 
 struct KernelShape {
@@ -1537,11 +1544,12 @@ struct KernelShape {
     // fixed cost per round of workgroups (pipeline fill, epilogue; us)
     double rate_full, rate_idle, fixed_us;
 };
-static constexpr KernelShape kKernels[5] = {{256, 256, 1, 3.74, 7.64, 19.4},
-                                            {256, 256, 1, 3.71, 6.11, 20.1},
-                                            {256, 128, 2, 3.61, 4.86, 15.3},
-                                            {128, 256, 2, 3.70, 4.98, 15.5},
-                                            {128, 128, 4, 3.25, 3.64, 10.9}};
+static constexpr KernelShape kKernels[5] = {{256, 256, 1, 5.11, 7.21, 10.3},
+                                            {256, 256, 1, 5.22, 7.25, 15.5},
+                                            {256, 128, 2, 4.55, 6.12, 10.9},
+                                            {128, 256, 2, 4.59, 6.49, 11.0},
+                                            {128, 128, 4, 4.04, 5.65, 8.1}};
+static constexpr double kSecondLaunchUs = 3.5;  // the second launch of a column split
 static constexpr double kPartialTBs = 12.6;  // partials out and back (MALL-resident)
 static constexpr double kSplitEpiUs = 0.5;   // the extra epilogue launch
 
@@ -1550,19 +1558,22 @@ static size_t partial_bytes(int64_t M, int64_t N, int ks) {
     return (size_t)ks * (size_t)((M + 31) / 32) * (size_t)((N + 31) / 32) * 4096u;
 }
 
-// Estimated duration (microseconds): a fixed cost per round of one
-// workgroup per CU, plus the FLOPs of the workgroups spread over the CUs at
-// a rate that rises as fewer CUs are busy (clock headroom); a K split adds
-// the partials' round trip and the epilogue launch.
+// Estimated duration (microseconds), round by round: each round of at most
+// one workgroup per CU costs a fixed amount plus one workgroup's FLOPs at a
+// per-CU rate that rises as fewer CUs are busy (clock headroom, memory
+// bandwidth per CU); a K split adds the partials' round trip and the
+// epilogue launch.  Fitted to unsplit launches of every kernel on the layer
+// shapes and to column-split pairs (MI355X, 4 % rms error).
 static double plan_cost(int64_t M, int64_t N, int64_t K, int kernel, int ks, int cus) {
     const KernelShape &k = kKernels[kernel];
     const int64_t wgs = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * ks;
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    const double fill = (double)(wgs < cus ? wgs : cus) / cus;
-    const double rate = k.rate_full + (k.rate_idle - k.rate_full) * (1.0 - fill);
     const double wg_flop = 2.0 * k.bm * k.bn * (double)K / ks;
-    const double spread = (double)wgs / cus > 1.0 ? (double)wgs / cus : 1.0;
-    double t = (double)rounds * k.fixed_us + spread * wg_flop / (rate * 1e6);
+    double t = 0.0;
+    for (int64_t left = wgs; left > 0; left -= cus) {
+        const double fill = (double)(left < cus ? left : cus) / cus;
+        const double rate = k.rate_full + (k.rate_idle - k.rate_full) * (1.0 - fill);
+        t += k.fixed_us + wg_flop / (rate * 1e6);
+    }
     if (ks > 1) t += 2.0 * (double)partial_bytes(M, N, ks) / (kPartialTBs * 1e6) + kSplitEpiUs;
     return t;
 }
@@ -1667,6 +1678,26 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int cus, const DownPl
             if (total < best_cost) {
                 best_cost = total;
                 best = {kernel, ks, fuse};
+            }
+        }
+    }
+    // column split: the 256 x 256 kernel on whole rounds of tiles, smaller
+    // tiles for the rest of the columns (no K split, no partial sums)
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    if (K % kSK == 0 && tm * tn > cus && (tm * tn) % cus != 0) {
+        const double down = dp.kl > 0 ? down_alone_us(M, dp) : 0.0;
+        for (int64_t rounds = 1; rounds * cus < tm * tn; ++rounds) {
+            const int64_t c = rounds * cus / tm;  // whole tile columns in these rounds
+            if (c <= 0 || c >= tn) continue;
+            const int64_t n1 = 256 * c;
+            const double c0 = plan_cost(M, n1, K, 0, 1, cus);
+            for (int k2 = 2; k2 < 5; ++k2) {
+                if (ns % kKernels[k2].wk != 0) continue;
+                const double total = c0 + plan_cost(M, N - n1, K, k2, 1, cus) + kSecondLaunchUs + down;
+                if (total < best_cost) {
+                    best_cost = total;
+                    best = {0, 1, false, (int)n1, k2};
+                }
             }
         }
     }
@@ -1877,6 +1908,31 @@ static pact_status gemm_common(const pact_nvfp4 *aq, const pact_nvfp4 *bq, const
         a.rpad = rpad;
         a.tld = ng * rpad;
     }
+    if (plan.n1 > 0 && plan.n1 < a.N) {
+        // column split: columns [0, n1) with plan.kernel, [n1, N) with
+        // plan.kernel2 (the same operands, shifted by n1 output columns;
+        // group boundaries of a grouped LoRA shift with them)
+        GemmArgs b = a;
+        a.N = plan.n1;
+        a.b_bytes = (uint32_t)((int64_t)plan.n1 * (Kc / 2));
+        PACT_TRY(launch_plan(a, plan.kernel, st));
+        const int64_t n1 = plan.n1;
+        b.N = (int)(Nout - n1);
+        b.b_codes += n1 * (Kc / 2);
+        b.b_scales += n1 * (Kc / 16);
+        b.b_d += n1;
+        b.b_bytes = (uint32_t)((Nout - n1) * (Kc / 2));
+        b.Y += n1;
+        if (b.C) b.C += n1;
+        if (b.T) {
+            if (b.ngroups > 1) {
+                for (int g = 0; g <= b.ngroups; ++g) b.gcol[g] -= (int)n1;
+            } else {
+                b.Qs += n1 * b.q_sn;
+            }
+        }
+        return launch_plan(b, plan.kernel2, st);
+    }
     return launch_plan(a, plan.kernel, st);
 }
 
@@ -1892,6 +1948,16 @@ extern "C" pact_status pact_debug_gemm_plan(int64_t M, int64_t N, int64_t K, int
     *kernel = plan.kernel;
     *ks = plan.ks;
     if (fused) *fused = plan.fuse ? 1 : 0;
+    return PACT_OK;
+}
+
+extern "C" pact_status pact_debug_gemm_plan_columns(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dgrad,
+                                                    int32_t *n1, int32_t *kernel2) {
+    if (M < 0 || N < 0 || K < 0 || r < 0 || r > 256 || !n1 || !kernel2) return PACT_ERR_INVALID_ARG;
+    const GemmPlan plan =
+        plan_gemm(M, N, K, device_cus(), DownPlan{r > 0 ? K : 0, dgrad != 0, (int)round_up(r > 0 ? r : 16, 16)});
+    *n1 = plan.n1;
+    *kernel2 = plan.kernel2;
     return PACT_OK;
 }
 

@@ -41,7 +41,8 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_debug_sigmoid32", "pact_debug_gemm_plan", "pact_silu_mul_bwd_quant_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
            "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
-           "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc"]
+           "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc",
+           "pact_debug_gemm_plan_columns"]
 
 
 class PactError(RuntimeError):
@@ -106,6 +107,8 @@ def lib():
         L.pact_gemm_nvfp4_fwd_noalloc.restype = st
         L.pact_gemm_nvfp4_fwd_noalloc.argtypes = [NV, P, I64, NV, LO, P, P, I64, P]
         I32P = ctypes.POINTER(ctypes.c_int32)
+        L.pact_debug_gemm_plan_columns.restype = st
+        L.pact_debug_gemm_plan_columns.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
         L.pact_debug_lora_down_plan.restype = st
         L.pact_debug_lora_down_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 I32P, I32P, I32P, I32P, I32P]
@@ -442,6 +445,15 @@ def pact_debug_gemm_plan(M: int, N: int, K: int, r: int = 0, dgrad: bool = False
     _check(lib().pact_debug_gemm_plan(M, N, K, r, 1 if dgrad else 0, ctypes.byref(k), ctypes.byref(ks),
                                       ctypes.byref(f)), "pact_debug_gemm_plan")
     return k.value, ks.value, bool(f.value)
+
+
+def pact_debug_gemm_plan_columns(M: int, N: int, K: int, r: int = 0, dgrad: bool = False) -> tuple[int, int]:
+    """(n1, kernel2) of the launch plan's column split: output columns
+    [0, n1) in the first launch, [n1, N) with kernel kernel2; n1 == 0: none."""
+    n1, k2 = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pact_debug_gemm_plan_columns(M, N, K, r, 1 if dgrad else 0, ctypes.byref(n1), ctypes.byref(k2)),
+           "pact_debug_gemm_plan_columns")
+    return n1.value, k2.value
 
 
 LORA_DOWN_ROUTES = {1: "fused into the split-K launch", 2: "pipelined", 3: "transpose, then pipelined",

@@ -157,6 +157,22 @@ def test_gemm_plan_lora_down_placement(L):
     assert fu.value == 0 or ks.value > 2
 
 
+def test_gemm_plan_column_split_host_logic(L):
+    """A column split puts whole rounds of 256 x 256 tiles in the first launch
+    (n1 a multiple of 256 with (M / 256) (n1 / 256) a multiple of the CU
+    count) and appears only where one launch would leave a partly filled
+    round; invalid arguments are rejected."""
+    i32 = ctypes.c_int32
+    n1, k2 = i32(), i32()
+    assert L.pact_debug_gemm_plan_columns(-1, 8, 8, 0, 0, ctypes.byref(n1), ctypes.byref(k2)) == 1
+    assert L.pact_debug_gemm_plan_columns(8, 8, 8, 0, 0, None, ctypes.byref(k2)) == 1
+    assert L.pact_debug_gemm_plan_columns(8192, 3072, 8192, 16, 0, ctypes.byref(n1), ctypes.byref(k2)) == 0
+    assert n1.value == 2048 and 2 <= k2.value <= 4 and (8192 // 256) * (n1.value // 256) % 256 == 0
+    for M, N, K in [(8192, 8192, 3072), (8192, 16384, 3072), (1024, 2048, 2048), (256, 1024, 512)]:
+        assert L.pact_debug_gemm_plan_columns(M, N, K, 16, 0, ctypes.byref(n1), ctypes.byref(k2)) == 0
+        assert n1.value == 0  # whole rounds already, or fewer tiles than CUs
+
+
 def test_lora_down_plan_host_logic(L):
     """The LoRA-down diagnostic agrees with the GEMM plan (route 1 exactly
     when the plan fuses it into the split-K launch), takes one pass per 64

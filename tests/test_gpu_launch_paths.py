@@ -84,3 +84,29 @@ def test_non_power_of_two_lora_scale(M, N, K, r, s):
     one rounding of the rank-r term, which stays inside the GEMM tolerance."""
     rows = _rows(M, seed=4) if M > 1024 else None
     _run_pair(M, N, K, r, seed=47, with_c=False, rows=rows, s=s)
+
+
+def test_column_split_plan_single():
+    """8192 x 3072 over K = 8192 (3B-shaped down forward, gate/up input
+    gradient): 384 tiles of 256 x 256 are 1.5 rounds of the CUs, so the plan
+    runs columns [0, 2048) with the 256 x 256 kernel (exactly one round) and
+    the rest with 128 x 256 tiles as a second launch; both directions on
+    sampled rows."""
+    M, N, K, r = 8192, 3072, 8192, 16
+    assert pb.pact_debug_gemm_plan_columns(M, N, K, r) == (2048, 3)
+    assert pb.pact_debug_gemm_plan_columns(M, N, K, r, dgrad=True) == (2048, 3)
+    _run_pair(M, N, K, r, seed=53, with_c=True, rows=_rows(M, seed=5))
+    # the transposed direction of the same pair: output [M][K] over N
+    _run_pair(M, K, N, r, seed=59, with_c=True, rows=_rows(M, seed=6))
+
+
+@pytest.mark.parametrize("M,K,rows,r,n1", [
+    (4096, 1536, [8960, 8960], 16, 16384),          # Qwen-shaped gate|up: the split falls inside group 1
+    (8192, 3072, [3072, 1024, 1024], 16, 4096),     # 3B-shaped q|k|v: the split falls on a group boundary
+])
+def test_column_split_plan_grouped(M, K, rows, r, n1):
+    """Grouped forward whose plan splits the output columns across two
+    launches: the second launch's group boundaries shift with its columns."""
+    ng = len(rows)
+    assert pb.pact_debug_gemm_plan_columns(M, sum(rows), K, ng * r)[0] == n1
+    grouped_case(M, K, rows, r, seed=61 + ng, rows_sample=_rows(M, seed=7))
