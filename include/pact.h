@@ -202,8 +202,9 @@ pact_status pact_gemm_nvfp4_dgrad(const pact_nvfp4 *dYq, const uint16_t *dY, int
                                   void *ws, size_t ws_bytes, void *stream);
 
 /* SiLU*mul backward from the NVFP4 gate/up stash (blog "Method", second
- * bullet: gate/up are kept in NVFP4 for backward; abstract: "saves gate/up
- * activations in NVFP4 for backward"):
+ * bullet, and the abstract of "PACT: NVFP4 Data-Flow LoRA Fine-Tuning on
+ * Consumer GPUs": the gate and up activations are kept in NVFP4 for the
+ * backward pass):
  *   g' = bf16(deq(gq)), u' = bf16(deq(uq))   (deq: code x block scale x row scale),
  *   du = bf16(fl32(dh sigma32(g'))),  dg = bf16(fl32(fl32(dh u') dsilu32(g'))),
  *   dgq = Q(dg), duq = Q(du)   (the operands of the gate/up input-gradient GEMMs),

@@ -39,6 +39,55 @@ def test_dsilu_table_against_float64():
     assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-15 * np.abs(ref) + 1e-300)
 
 
+def test_dsilu_exhaustive_against_mpmath():
+    """silu'_32(g) = binary32 rounding of sigma(g)(1 + g(1 - sigma(g))) for
+    every finite BF16 g, against 50-digit mpmath evaluation (100 digits when
+    the 50-digit value lies within 1e-40 relative of a binary32 rounding
+    midpoint); outside |g| <= 128 the value is 1 (g > 128: the excess over 1,
+    about g e^-g, is far below half an ulp) or -0 (g < -128: about g e^g, far
+    below the smallest subnormal)."""
+    import math
+    from fractions import Fraction
+
+    import mpmath
+
+    from tests import _exact as ex
+
+    t = oracle.dsilu_table()
+
+    def dsilu_mp(gv, dps):
+        mpmath.mp.dps = dps
+        gm = mpmath.mpf(gv)
+        sg = 1 / (1 + mpmath.exp(-gm))
+        return sg * (1 + gm * (1 - sg))
+
+    def frac(v):
+        if v == 0:
+            return Fraction(0)
+        man, exp = mpmath.mpf(v).man_exp
+        mag = Fraction(int(man)) * Fraction(2) ** int(exp)
+        return -mag if v < 0 else mag
+
+    for b in _finite_bf16():
+        gv = float(_f32(np.array([b]))[0])
+        got = float(t[b])
+        if gv > 128:
+            assert got == 1.0, (hex(b), gv, got)
+            continue
+        if gv < -128:
+            assert got == 0.0 and math.copysign(1.0, got) < 0, (hex(b), gv, got)
+            continue
+        v = frac(dsilu_mp(gv, 50))
+        want = ex.rn32(v)
+        # distance to the midpoints next to the rounded value, relative
+        if want != 0:
+            up = ex.rn32(want + abs(want) * Fraction(1, 2 ** 23))
+            mids = [(want + up) / 2, want - (up - want) / 2]
+            if min(abs(v - m) for m in mids) <= abs(want) * Fraction(1, 10 ** 40):
+                want = ex.rn32(frac(dsilu_mp(gv, 100)))
+        assert Fraction(got) == want, (hex(b), gv, got, float(want))
+
+
 def test_dsilu_identities_and_limits():
     t = oracle.dsilu_table()
     assert t[0x0000] == 0.5 and t[0x8000] == 0.5           # silu'(+-0) = 1/2
