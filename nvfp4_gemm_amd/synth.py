@@ -158,3 +158,14 @@ def layer_inputs(shape: LayerShape, seed: int = 0, layer: int = 0, M: int | None
             li.A[nm] = normal_bf16(g[5 + 3 * i], (shape.rank, k), 0.02)
             li.B[nm] = normal_bf16(g[6 + 3 * i], (n, shape.rank), 0.01)
     return li
+
+
+def calibration_bf16(rng, n, K, nu=4.0, scale=0.5, rank=32, mix=1.0):
+    """Calibration activations [n, K] for the offline weight calibration:
+    Student-t(nu) * scale noise plus a shared low-rank component (rank
+    N(0, 1) factors with N(0, (scale mix)^2 / rank) loadings), so that the
+    columns are correlated as a layer's inputs are."""
+    Z = rng.standard_t(nu, size=(n, K)) * scale
+    F = rng.standard_normal((n, rank))
+    P = rng.standard_normal((rank, K)) * (scale * mix / np.sqrt(rank))
+    return to_bf16_bits(Z + F @ P)

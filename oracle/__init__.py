@@ -91,6 +91,7 @@ def lib():
         L.orc_adamw_step.argtypes = [P, P, P, P, I64, D, D, D, D, D, I64]
         L.orc_master_bf16.argtypes = [P, I64, P]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_gptq_sweep.argtypes = [P, P, P, I64, I64, ctypes.c_int32, P, P]
         _lib = L
     return _lib
 
@@ -376,4 +377,60 @@ def bf16_of_master(p) -> np.ndarray:
     x = np.ascontiguousarray(np.asarray(p, dtype=np.float64))
     out = np.empty(x.shape, np.uint16)
     lib().orc_master_bf16(_p(x), x.size, _p(out))
+    return out
+
+
+# ---- NVFP4-adapted GPTQ (blog "Method", bullet 3; arXiv abstract) ---------
+# Offline calibration of a frozen weight W [N, K] from calibration activations
+# X [n, K]: the Hessian of the layer's output error is taken over the
+# reconstructed NVFP4 activations X^ = deq(Q(X)) (the GEMM's actual input),
+# H = (2/n) X^T X^; GPTQ (Frantar et al.) then quantizes W column by column,
+# spreading each column's rounding error over the columns not yet quantized
+# through the upper Cholesky factor of H^-1.  Linear algebra in binary64
+# (numpy's matmul, Cholesky and inverse as library steps); the sweep is the
+# C function orc_gptq_sweep.
+
+def gptq_hessian(xq: NVFP4, scale: float | None = None) -> np.ndarray:
+    """H = scale X^T X (binary64) over the dequantized NVFP4 rows X of xq;
+    scale defaults to 2/n (n = rows of xq)."""
+    X = dequantize(xq).astype(np.float64)
+    if scale is None:
+        scale = 2.0 / max(X.shape[0], 1)
+    return scale * (X.T @ X)
+
+
+def gptq_inverse_factor(H: np.ndarray, percdamp: float = 0.01):
+    """GPTQ's preparation of H (copied): columns with zero diagonal are dead
+    (their diagonal set to 1, their weights to 0); percdamp times the mean
+    diagonal is added to the diagonal; then U, the upper Cholesky factor of
+    H^-1 (H^-1 = U^T U), through H = L L^T, H^-1 = L^-T L^-1.
+    Returns (U, dead mask)."""
+    H = np.array(H, dtype=np.float64, copy=True)
+    K = H.shape[0]
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    damp = percdamp * np.mean(np.diag(H))
+    H[np.arange(K), np.arange(K)] += damp
+    L = np.linalg.cholesky(H)
+    Linv = np.linalg.inv(L)
+    Hinv = Linv.T @ Linv
+    U = np.linalg.cholesky(Hinv).T
+    return np.ascontiguousarray(U), dead
+
+
+def gptq_nvfp4(W: np.ndarray, H: np.ndarray, blocksize: int = 128, percdamp: float = 0.01) -> NVFP4:
+    """NVFP4 forward layout of the BF16 weight W [N, K] calibrated by GPTQ
+    with Hessian H [K, K]: row scales d of the plain quantizer (from W's row
+    maxima), block scales and codes chosen column by column by the sweep."""
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    rtn = quantize_bf16(W)  # row scales d = fl32(max|w| / 2688)
+    U, dead = gptq_inverse_factor(H, percdamp)
+    Wd = bf16_to_f32(W).astype(np.float64)
+    Wd[:, dead] = 0.0
+    Wd = np.ascontiguousarray(Wd)
+    out = NVFP4.empty(N, K)
+    out.d[:] = rtn.d
+    lib().orc_gptq_sweep(_p(U), _p(Wd), _p(_c(out.d, np.float32)), N, K, int(blocksize), _p(out.codes),
+                         _p(out.scales))
     return out

@@ -767,3 +767,76 @@ void orc_adamw_step(double *p, double *m, double *v, const double *g, int64_t n,
         p[i] = p[i] - lr * mhat / (sqrt(vhat) + eps);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4-adapted GPTQ: the column sweep ([blog] Method, bullet 3: the frozen */
+/* weights are calibrated offline by GPTQ adapted to the NVFP4 block scales,  */
+/* with statistics from reconstructed NVFP4 activations; arXiv abstract).     */
+/* GPTQ (Frantar et al.) quantizes the columns of W [N][K] in order and       */
+/* spreads each column's rounding error over the columns not yet quantized,   */
+/* through the upper Cholesky factor U of the inverse Hessian (H^-1 = U^T U): */
+/*   err = (w_i - q_i) / U[i][i];  w_j -= err U[i][j]  (j > i).                */
+/* Updates inside a block of `bs` columns are applied column by column; the   */
+/* block's errors reach the later columns at the block's end, as one sum over */
+/* the block's columns in increasing order (GPTQ's lazy batch update; the     */
+/* same result as column by column up to the rounding order).                 */
+/* NVFP4: at the first column of every 16-column block the block's E4M3 scale */
+/* is chosen by the plain quantizer's rule on the current (error-updated)     */
+/* weights rounded to binary32, with the row scale d of the original weights; */
+/* each column's code is the plain quantizer's code of its binary32-rounded   */
+/* current weight under that scale; q = code value x scale x d (exact in      */
+/* binary64).  Rows are independent (OpenMP over rows).                      */
+/* ------------------------------------------------------------------------- */
+void orc_gptq_sweep(const double *U, double *W, const float *d, int64_t N, int64_t K, int32_t bs,
+                    uint8_t *codes, uint8_t *scales) {
+    assert(K % 16 == 0 && bs % 16 == 0 && bs > 0);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        double *w = W + n * K;
+        uint8_t *cr = codes + n * (K / 2);
+        uint8_t *sr = scales + n * (K / 16);
+        const float dn = d[n];
+        const float D = 6.0f * dn;
+        double *err = (double *)malloc(sizeof(double) * (size_t)bs);
+        float S = 0.0f;
+        for (int64_t i1 = 0; i1 < K; i1 += bs) {
+            const int64_t i2 = i1 + bs < K ? i1 + bs : K;
+            for (int64_t i = i1; i < i2; ++i) {
+                if (i % 16 == 0) {
+                    /* the block's scale from its current weights */
+                    float amax = 0.0f;
+                    for (int64_t j = i; j < i + 16; ++j) {
+                        const float a = fabsf((float)w[j]);
+                        if (a > amax) amax = a;
+                    }
+                    uint8_t sb = 0;
+                    if (dn != 0.0f) {
+                        const float t = amax / D;
+                        sb = orc_e4m3_encode(t);
+                    }
+                    sr[i / 16] = sb;
+                    S = orc_e4m3_value(sb) * dn;
+                }
+                const float wf = (float)w[i];
+                uint8_t mag = 0;
+                if (S != 0.0f) mag = orc_e2m1_encode_mag(fabsf(wf) / S);
+                const uint8_t code = (uint8_t)((signbit(wf) ? 8 : 0) | mag);
+                if (i & 1)
+                    cr[i / 2] |= (uint8_t)(code << 4);
+                else
+                    cr[i / 2] = code;
+                const double q = (double)orc_e2m1_value(code) * (double)orc_e4m3_value(sr[i / 16]) * (double)dn;
+                const double e = (w[i] - q) / U[i * K + i];
+                err[i - i1] = e;
+                for (int64_t j = i + 1; j < i2; ++j) w[j] -= e * U[i * K + j];
+                w[i] = q;
+            }
+            for (int64_t j = i2; j < K; ++j) {
+                double s = 0.0;
+                for (int64_t i = i1; i < i2; ++i) s += err[i - i1] * U[i * K + j];
+                w[j] -= s;
+            }
+        }
+        free(err);
+    }
+}

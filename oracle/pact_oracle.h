@@ -125,6 +125,14 @@ void orc_lora_grads(const uint8_t *xc, const uint8_t *xs, const float *xd, int64
                     const uint16_t *dY, int64_t ld_dy, int64_t N, const uint16_t *A, const uint16_t *B,
                     int32_t r, float s, double *dA, double *dB);
 
+/* ---- NVFP4-adapted GPTQ ([blog] Method, bullet 3; [abs]) ----
+ * The column sweep of GPTQ over W [N][K] (binary64, destroyed: on return it
+ * holds the quantized values) with the upper Cholesky factor U [K][K] of the
+ * inverse Hessian, lazy batches of bs columns, and the NVFP4 block rule with
+ * the given row scales d [N]: codes [N][K/2], scale bytes [N][K/16]. */
+void orc_gptq_sweep(const double *U, double *W, const float *d, int64_t N, int64_t K, int32_t bs,
+                    uint8_t *codes, uint8_t *scales);
+
 int orc_num_threads(void);
 
 #ifdef __cplusplus
