@@ -272,6 +272,38 @@ pact_status pact_lora_grads_nvfp4(const pact_nvfp4 *Xq, const uint16_t *dY, int6
 pact_status pact_adamw_step(float *p, float *m, float *v, const float *g, uint16_t *w, int64_t n, float lr,
                             float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream);
 
+/* NVFP4-adapted GPTQ, offline calibration of a frozen weight (blog "Method",
+ * third bullet, and the arXiv abstract: GPTQ adapted to the NVFP4 block
+ * scales, with statistics from reconstructed NVFP4 activations; GPTQ is
+ * Frantar et al.).  Two calls:
+ *
+ * pact_gptq_hessian_nvfp4: H = scale X^T X (+ H when accumulate != 0) in
+ * binary64, X [n][K] the dequantized values of the NVFP4 calibration rows Xq
+ * (fl32(code x block scale x row scale)); GPTQ's Hessian is scale = 2/n.
+ * H: device, [K][K] row-major binary64, 16-byte aligned.  Xq->cols % 16 == 0.
+ *
+ * pact_gptq_nvfp4: the forward NVFP4 layout W_fwd [N][K] of the BF16 weight
+ * W [N][K] (leading dimension ld_w) calibrated with H [K][K]: columns whose
+ * diagonal is 0 are dead (weights set to 0); percdamp times the mean diagonal
+ * is added to the diagonal; U, the upper Cholesky factor of H^-1, spreads
+ * each column's rounding error over the later columns, in lazy batches of
+ * `blocksize` columns (16..128, a multiple of 16).  Row scales are the plain
+ * quantizer's (max|w| of the original row / 2688); at the first column of
+ * every 16-column block the block's E4M3 scale is the plain quantizer's rule
+ * on the block's current weights rounded to binary32; each code is the plain
+ * quantizer's code of the current weight rounded to binary32.  H is used as
+ * scratch (overwritten).  K % 64 == 0 (else PACT_ERR_UNSUPPORTED_SHAPE);
+ * workspace of pact_gptq_workspace(N, K) bytes (2 K^2 + N K + 64 K binary64
+ * values and change; PACT_ERR_WORKSPACE when smaller).  The result feeds
+ * pact_build_weight_layouts(W = NULL, W_fwd_in = W_fwd) for the transposed
+ * layout.  If H (after dampening) is not numerically positive definite the
+ * output is unspecified. */
+pact_status pact_gptq_hessian_nvfp4(const pact_nvfp4 *Xq, double scale, int32_t accumulate, double *H,
+                                    void *stream);
+size_t pact_gptq_workspace(int64_t N, int64_t K);
+pact_status pact_gptq_nvfp4(const uint16_t *W, int64_t ld_w, int64_t N, int64_t K, double *H, double percdamp,
+                            int32_t blocksize, const pact_nvfp4 *W_fwd, void *ws, size_t ws_bytes, void *stream);
+
 /* Forward GEMM for callers that cannot allocate device memory (code under
  * stream capture, tight serving loops, harnesses that forbid allocation):
  * pact_gemm_nvfp4_fwd with the same arguments and results, but its workspace

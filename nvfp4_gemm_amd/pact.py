@@ -42,7 +42,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
            "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
            "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc",
-           "pact_debug_gemm_plan_columns"]
+           "pact_debug_gemm_plan_columns", "pact_gptq_hessian_nvfp4", "pact_gptq_workspace", "pact_gptq_nvfp4"]
 
 
 class PactError(RuntimeError):
@@ -102,6 +102,13 @@ def lib():
         L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]
+        D = ctypes.c_double
+        L.pact_gptq_hessian_nvfp4.restype = st
+        L.pact_gptq_hessian_nvfp4.argtypes = [NV, D, ctypes.c_int32, P, P]
+        L.pact_gptq_workspace.restype = ctypes.c_size_t
+        L.pact_gptq_workspace.argtypes = [I64, I64]
+        L.pact_gptq_nvfp4.restype = st
+        L.pact_gptq_nvfp4.argtypes = [P, I64, I64, I64, P, D, ctypes.c_int32, NV, P, ctypes.c_size_t, P]
         L.pact_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.pact_noalloc_scratch_bytes.argtypes = []
         L.pact_gemm_nvfp4_fwd_noalloc.restype = st
@@ -296,6 +303,39 @@ def pact_gemm_nvfp4_fwd(Xq: NVFP4Tensor, W_fwd: NVFP4Tensor, X=None, lora: LoRA 
     """Y = bf16(d_x d_w Xq.W_fwd^T + s bf16(X A^T) B^T (+ C))."""
     return _gemm(lib().pact_gemm_nvfp4_fwd, "pact_gemm_nvfp4_fwd", Xq, X, W_fwd, lora, C, Y, ws,
                  stream)
+
+
+def pact_gptq_hessian_nvfp4(Xq: NVFP4Tensor, H=None, scale: float | None = None, accumulate: bool = False,
+                            stream=None):
+    """H [K][K] float64 = scale X^T X (+ H when accumulate) over the
+    dequantized NVFP4 rows of Xq; scale defaults to 2 / rows."""
+    K = Xq.cols
+    if H is None:
+        H = torch.empty((K, K), dtype=torch.float64, device=Xq.codes.device)
+    if scale is None:
+        scale = 2.0 / max(Xq.rows, 1)
+    d = Xq.desc()
+    _check(lib().pact_gptq_hessian_nvfp4(ctypes.byref(d), float(scale), 1 if accumulate else 0, _ptr(H),
+                                         _stream(stream)), "pact_gptq_hessian_nvfp4")
+    return H
+
+
+def pact_gptq_workspace(N: int, K: int) -> int:
+    return int(lib().pact_gptq_workspace(N, K))
+
+
+def pact_gptq_nvfp4(W, H, percdamp: float = 0.01, blocksize: int = 128, W_fwd: NVFP4Tensor | None = None,
+                    ws=None, stream=None) -> NVFP4Tensor:
+    """GPTQ-calibrated forward NVFP4 layout of the BF16 weight W [N][K] with
+    Hessian H [K][K] (float64; overwritten as scratch)."""
+    N, K = W.shape
+    W_fwd = W_fwd if W_fwd is not None else NVFP4Tensor.empty(N, K, W.device)
+    if ws is None:
+        ws = torch.empty((max(pact_gptq_workspace(N, K), 16),), dtype=torch.uint8, device=W.device)
+    d = W_fwd.desc()
+    _check(lib().pact_gptq_nvfp4(_ptr(W), _ld(W), N, K, _ptr(H), float(percdamp), int(blocksize), ctypes.byref(d),
+                                 _ptr(ws), ws.numel(), _stream(stream)), "pact_gptq_nvfp4")
+    return W_fwd
 
 
 def pact_noalloc_scratch_bytes() -> int:

@@ -217,6 +217,29 @@ def test_noalloc_gemm_rejects_oversized_lora_product(L):
     assert L.pact_gemm_nvfp4_fwd_noalloc(None, 16, 256, ctypes.byref(w), None, None, 16, 64, None) == 1
 
 
+def test_gptq_validation(L):
+    """The GPTQ entry points reject bad arguments before any device work."""
+    D = ctypes.c_double
+    x = pb.pact_nvfp4(16, 16, 16, 32, 256)
+    assert L.pact_gptq_hessian_nvfp4(None, D(1.0), 0, 16, None) == 1
+    assert L.pact_gptq_hessian_nvfp4(ctypes.byref(x), D(1.0), 0, None, None) == 1
+    x_bad = pb.pact_nvfp4(16, 16, 16, 32, 40)
+    assert L.pact_gptq_hessian_nvfp4(ctypes.byref(x_bad), D(1.0), 0, 16, None) == 2
+    assert L.pact_gptq_hessian_nvfp4(ctypes.byref(x), D(1.0), 0, 8, None) == 3  # H misaligned
+    N, K = 32, 256
+    need = L.pact_gptq_workspace(N, K)
+    assert need >= 8 * (2 * K * K + N * K)
+    w = pb.pact_nvfp4(16, 16, 16, N, K)
+    call = lambda K_=K, bs=128, ws_bytes=need, damp=0.01, Wp=16, wd=w: L.pact_gptq_nvfp4(
+        Wp, K_, N, K_, 16, D(damp), bs, ctypes.byref(wd), 16, ws_bytes, None)
+    assert call(bs=8) == 1 and call(bs=256) == 1 and call(damp=-1.0) == 1
+    assert call(bs=40) == 2                                  # not a multiple of 16
+    w2 = pb.pact_nvfp4(16, 16, 16, N, 272)
+    assert call(K_=272, wd=w2, ws_bytes=L.pact_gptq_workspace(N, 272)) == 2   # K % 64 != 0
+    assert call(ws_bytes=need - 1) == 4
+    assert call(Wp=None) == 1
+
+
 def test_backward_validation(L):
     """Argument checks of the backward entry points (host only, nothing is
     launched on an error)."""
