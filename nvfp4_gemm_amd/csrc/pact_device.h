@@ -145,11 +145,27 @@ __device__ __forceinline__ RowQ row_params(float amax) {
     return r;
 }
 
+// row_params for an amax exactly representable in BF16 (a maximum of BF16
+// magnitudes): fl32(amax / 2688) as the binary64 product with RN64(1/2688),
+// equal to the correctly rounded quotient by the argument at quot_bf16.
+__device__ __forceinline__ RowQ row_params_bf16(float amax) {
+    RowQ r;
+    r.d = quot_bf16(amax, 1.0 / 2688.0);
+    r.D = 6.0f * r.d;
+    r.rD = r.d == 0.0f ? 0.0 : 1.0 / (double)r.D;
+    return r;
+}
+
 // Two BF16 values per 32-bit word: packed 16-bit integer helpers.
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+}
+
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a),
                                                                   __builtin_bit_cast(u16x2_t, b)));
 }
 
@@ -222,6 +238,15 @@ __device__ __forceinline__ void encode_block16(const float v[16], float bamax, R
     }
     codes_lo = w[0];
     codes_hi = w[1];
+}
+
+// A kernel's by-value argument struct read in place from the kernel-argument
+// segment: every field is a scalar load the compiler may repeat where needed,
+// rather than a copy it keeps live in scalar registers (or in scratch, where
+// a field's address is taken).
+template <class T>
+__device__ __forceinline__ const T &kernel_args() {
+    return *(const T *)(const __attribute__((address_space(4))) T *)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
 // ---- wavefront reductions (64 lanes) --------------------------------------

@@ -7,8 +7,8 @@
 // what backward keeps; forward nonlinear ops read BF16.)
 //
 // Design: one row per 64*WPR threads; each thread owns whole 16-element blocks
-// (blocks lane, lane + T, ...), loaded with two 16-byte loads and kept in
-// registers as packed BF16, so the row is read from HBM exactly once.  Block
+// (lane, lane + T, ...; moved in 64-block chunks, see load_chunk), kept in registers
+// as packed BF16, so the row is read from HBM exactly once.  Block
 // and row maxima are taken on the packed words (magnitude bits compare as
 // integers); the row maximum (and, for RMSNorm, the sum of squares) is reduced
 // across the wavefront with shuffles and across the row's wavefronts through
@@ -101,9 +101,10 @@ __device__ __forceinline__ float silu32_select(uint32_t b, uint32_t t) {
 // offset of a pattern is its magnitude bits minus 102 << 7 (one packed 16-bit
 // subtraction per pair); offsets of 4096 and above (or wrapped below zero)
 // mark values outside the table's range, which take the closed rule, a path
-// a wavefront enters only when one of its lanes holds such a value.  All
-// table reads are issued before any is used; the empty asm keeps the compiler
-// from moving them into branches.
+// a wavefront enters only when one of its lanes holds such a value (the
+// forward's gate is a GEMM output, where exact zeros are rare).  All table
+// reads are issued before any is used; the empty asm keeps the compiler from
+// moving them into branches.
 __device__ __forceinline__ void silu32_x16(const uint32_t w[8], const uint32_t *tab, float s[16]) {
     uint32_t t[16];
     uint32_t oor = 0u;
@@ -129,6 +130,45 @@ __device__ __forceinline__ void silu32_x16(const uint32_t w[8], const uint32_t *
     }
 }
 
+// The SiLU backward reads g' = bf16 of a decoded NVFP4 value, which is exactly
+// zero for every zero code.  Its LDS table is laid out by (offset, sign) and
+// interleaved: entry 2k + s holds {sigma32, dsilu32} of the pattern with sign
+// s and magnitude bits (102 << 7) + k, k < 4096 (exponents 102..133), and
+// entries 8192 and 8193 those of +0 and -0 (+-0 and 0.5), so that zeros stay
+// on the fast path.
+constexpr int kSigTabZ = kSigTab + 2;
+
+__device__ __forceinline__ int silu_tab_source(int i) { return ((i & 1) << 12) | (i >> 1); }
+
+__device__ __forceinline__ void load_silu_dsilu_table_z(u32x2 *tab, int tid, int nthreads) {
+    for (int i = tid; i < kSigTabZ; i += nthreads) {
+        u32x2 e;
+        e.x = i < kSigTab ? kSigmoidCompact[silu_tab_source(i)] : (i == kSigTab ? 0u : 0x80000000u);
+        e.y = i < kSigTab ? kDsiluCompact[silu_tab_source(i)] : 0x3F000000u;  // 0.5f
+        tab[i] = e;
+    }
+}
+
+// Table entries of the two BF16 patterns packed in w (low half first), with
+// one packed 16-bit subtraction and clamp for both: magnitudes outside the
+// table's range map to the zero entries.  mx collects the largest magnitude,
+// mn the smallest magnitude minus one (zero wraps to 0xFFFF), for silu_tab_miss.
+__device__ __forceinline__ void silu_tab_entries(uint32_t w, uint32_t &ilo, uint32_t &ihi, uint32_t &mx,
+                                                 uint32_t &mn) {
+    const uint32_t mag = w & 0x7FFF7FFFu;
+    mx = pk_max_u16(mx, mag);
+    mn = pk_min_u16(mn, pk_sub_u16(mag, 0x00010001u));
+    const uint32_t rc = pk_min_u16(pk_sub_u16(mag, 0x33003300u), 0x10001000u);  // 0x3300 = 102 << 7
+    ilo = ((rc & 0xFFFFu) << 1) | ((w >> 15) & 1u);
+    ihi = ((rc >> 16) << 1) | (w >> 31);
+}
+
+// Whether some value seen by silu_tab_entries is neither zero nor in the
+// table's range (exponent below 102, or 134 and above, Inf and NaN included).
+__device__ __forceinline__ bool silu_tab_miss(uint32_t mx, uint32_t mn) {
+    return max(mx & 0xFFFFu, mx >> 16) >= 0x4300u || min(mn & 0xFFFFu, mn >> 16) < 0x32FFu;
+}
+
 // dsilu32 of a BF16 pattern b given its (always in-range) table entry t.
 __device__ __forceinline__ float dsilu32_select(uint32_t b, uint32_t t) {
     const uint32_t e = (b >> 7) & 0xFFu;
@@ -137,34 +177,91 @@ __device__ __forceinline__ float dsilu32_select(uint32_t b, uint32_t t) {
     return e < 102u ? 0.5f : (e < 134u ? __uint_as_float(t) : hi);
 }
 
+// sigma32 and dsilu32 of the 16 BF16 values packed in w[8] from the
+// interleaved table (each entry {sigma32, dsilu32}: one 8-byte LDS read serves
+// both), with the fast path of silu32_x16.
+__device__ __forceinline__ void silu_dsilu_x16(const uint32_t w[8], const u32x2 *tab, float s[16], float ds[16]) {
+    uint32_t ts[16], td[16];
+    uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t ilo, ihi;
+        silu_tab_entries(w[j], ilo, ihi, mx, mn);
+        const u32x2 lo = tab[ilo], hi = tab[ihi];
+        ts[2 * j] = lo.x;
+        td[2 * j] = lo.y;
+        ts[2 * j + 1] = hi.x;
+        td[2 * j + 1] = hi.y;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(ts[j]), "+v"(td[j]));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        s[j] = __uint_as_float(ts[j]);
+        ds[j] = __uint_as_float(td[j]);
+    }
+    if (silu_tab_miss(mx, mn)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s[2 * j] = silu32_select(w[j] & 0xFFFFu, ts[2 * j]);
+            s[2 * j + 1] = silu32_select(w[j] >> 16, ts[2 * j + 1]);
+            ds[2 * j] = dsilu32_select(w[j] & 0xFFFFu, td[2 * j]);
+            ds[2 * j + 1] = dsilu32_select(w[j] >> 16, td[2 * j + 1]);
+        }
+    }
+}
+
 // Workgroup barrier ordering LDS only.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int WPR>
-__device__ __forceinline__ void row_max3(float &a, float &b, float &c, float (*red)[4], int wave,
-                                         int lrow) {
-    a = wave_max(a);
-    b = wave_max(b);
-    c = wave_max(c);
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);  // every lane is active
+}
+
+// Maximum over the wavefront of two packed 16-bit unsigned values, in every
+// lane: four DPP steps within 16-lane rows, then lane swaps across rows.
+__device__ __forceinline__ uint32_t wave_max_pk_u16(uint32_t v) {
+    v = pk_max_u16(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]: lane i ^ 1
+    v = pk_max_u16(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]: lane i ^ 2
+    v = pk_max_u16(v, dpp_mov<0x141>(v));  // row_half_mirror: 8-lane groups
+    v = pk_max_u16(v, dpp_mov<0x140>(v));  // row_mirror: 16-lane rows
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 0 and 1, 2 and 3
+    v = pk_max_u16(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // the two halves
+    return pk_max_u16(b[0], b[1]);
+}
+
+// Row maxima of NV (1..3) non-negative BF16-exact values (maxima of block
+// maxima), two packed per 32-bit word (BF16 patterns of non-negative values
+// order as the values do), reduced across the wavefront and then across the
+// row's wavefronts through LDS in a fixed order, so that every thread of the
+// row sees the same values.
+template <int WPR, int NV>
+__device__ __forceinline__ void row_max(float &a, float &b, float &c, uint32_t (*red)[2], int wave, int lrow) {
+    uint32_t w0 = (__float_as_uint(a) >> 16) | (NV > 1 ? (__float_as_uint(b) & 0xFFFF0000u) : 0u);
+    uint32_t w1 = NV > 2 ? (__float_as_uint(c) >> 16) : 0u;
+    w0 = wave_max_pk_u16(w0);
+    if constexpr (NV > 2) w1 = wave_max_pk_u16(w1);
     if constexpr (WPR > 1) {
         if ((threadIdx.x & 63) == 0) {
-            red[wave][0] = a;
-            red[wave][1] = b;
-            red[wave][2] = c;
+            red[wave][0] = w0;
+            red[wave][1] = w1;
         }
         lds_sync();
-        const int w0 = lrow * WPR;
-        a = red[w0][0];
-        b = red[w0][1];
-        c = red[w0][2];
+        const int f = lrow * WPR;
+        w0 = red[f][0];
+        w1 = red[f][1];
 #pragma unroll
         for (int w = 1; w < WPR; ++w) {
-            a = fmaxf(a, red[w0 + w][0]);
-            b = fmaxf(b, red[w0 + w][1]);
-            c = fmaxf(c, red[w0 + w][2]);
+            w0 = pk_max_u16(w0, red[f + w][0]);
+            if constexpr (NV > 2) w1 = pk_max_u16(w1, red[f + w][1]);
         }
         lds_sync();
     }
+    a = __uint_as_float(w0 << 16);
+    if constexpr (NV > 1) b = __uint_as_float(w0 & 0xFFFF0000u);
+    if constexpr (NV > 2) c = __uint_as_float(w1 << 16);
 }
 
 // Hides the packed words from the compiler so that the encode phase unpacks
@@ -189,30 +286,50 @@ __device__ __forceinline__ void unpack16(const uint32_t w[8], float v[16]) {
 // per call within the layer step), although nontemporal loads had been 1.6x
 // faster on 8192 x 8192 inputs with the caches flushed.  Stores keep the
 // nontemporal hint.
-// base: row start (uniform across the wavefront); off: byte offset of the block.
-__device__ __forceinline__ void load_block(const uint16_t *base, uint32_t off, uint32_t w[8]) {
-    const char *p = reinterpret_cast<const char *>(base) + off;
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 16);
+// Row blocks move between HBM and registers with fully coalesced 16-byte
+// accesses.  A wavefront covers a chunk of 64 consecutive 16-element blocks
+// (2 KB of BF16) with two instructions: in the first, lanes i and 32 + i read
+// the two halves of block i (i < 32), in the second those of block 32 + i.
+// One v_permlane32_swap per register pair (upper lanes of the first with the
+// lower lanes of the second) then leaves lane l with block l of the chunk
+// whole.  The alternative, each lane reading its own 32-byte block with two
+// 16-byte accesses, has every instruction touch half of each cache line: on
+// the MI355X a 3:5 read:write stream ran 1.7x slower that way (3.3 against
+// 5.5 TB/s), a copy 1.2x.  Both helpers run in wavefront-uniform control flow
+// (the swap takes all lanes); `active` (uniform) and the block bound mask the
+// accesses, and masked loads yield zeros.  base: row start; cb: the chunk's
+// first block (a multiple of 64).
+__device__ __forceinline__ void swap_halves(u32x4 &a, u32x4 &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a[j], b[j], false, false);
+        a[j] = r[0];
+        b[j] = r[1];
+    }
+}
+
+__device__ __forceinline__ void load_chunk(const uint16_t *base, int cb, int nb, bool active, uint32_t w[8]) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31;
+    const char *p = reinterpret_cast<const char *>(base) + 32u * (uint32_t)(cb + i) + 16u * (uint32_t)(lane >> 5);
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (active && cb + i < nb) a = *reinterpret_cast<const u32x4 *>(p);
+    if (active && cb + 32 + i < nb) b = *reinterpret_cast<const u32x4 *>(p + 1024);
+    swap_halves(a, b);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-__device__ __forceinline__ void load_block_cached(const uint16_t *base, uint32_t off, uint32_t w[8]) {
-    const char *p = reinterpret_cast<const char *>(base) + off;
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(p + 16);
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-}
-
-__device__ __forceinline__ void store_block(uint16_t *base, uint32_t off, const uint32_t w[8]) {
-    char *p = reinterpret_cast<char *>(base) + off;
+__device__ __forceinline__ void store_chunk(uint16_t *base, int cb, int nb, bool active, const uint32_t w[8]) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 31;
     u32x4 a, b;
     a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
     b.x = w[4]; b.y = w[5]; b.z = w[6]; b.w = w[7];
-    __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(p));
-    __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(p + 16));
+    swap_halves(a, b);
+    char *p = reinterpret_cast<char *>(base) + 32u * (uint32_t)(cb + i) + 16u * (uint32_t)(lane >> 5);
+    if (active && cb + i < nb) __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(p));
+    if (active && cb + 32 + i < nb) __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(p + 1024));
 }
 
 __device__ __forceinline__ void emit_block(const NV &q, int64_t row, int cols, int b, const float v[16],
@@ -233,17 +350,20 @@ template <int WPR>
 constexpr int row_threads() { return WPR > 4 ? 64 * WPR : 256; }
 
 template <int WPR, int BPL, int MODE>
-__global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
+__global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a_arg) {
+    const RowArgs &a = kernel_args<RowArgs>();
+    (void)a_arg;
     constexpr int NT = row_threads<WPR>();
     constexpr int T = 64 * WPR;
     constexpr int RPW = NT / T;
-    __shared__ float red[NT / 64][4];
+    __shared__ uint32_t red[NT / 64][2];
     __shared__ double redd[NT / 64][2];
     __shared__ uint32_t sig[MODE == MODE_SILU ? kSigTab : 1];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lrow = tid / T;
     const int lt = tid % T;
+    const int c0 = lt & ~63;  // this wavefront's first chunk in the row (lane l: block c0 + l)
     const int cols = a.cols;
     const int nb = cols >> 4;
     if constexpr (MODE == MODE_SILU) {
@@ -266,12 +386,10 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
     bool valid[BPL];
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
-        const int b = lt + T * i;
-        valid[i] = active && b < nb;
-        if (valid[i]) {
-            load_block(xr, 32u * (uint32_t)b, xw[i]);
-            if constexpr (MODE == MODE_SILU) load_block(ur, 32u * (uint32_t)b, uw[i]);
-        }
+        const int cb = c0 + T * i;
+        valid[i] = active && lt + T * i < nb;
+        load_chunk(xr, cb, nb, active, xw[i]);
+        if constexpr (MODE == MODE_SILU) load_chunk(ur, cb, nb, active, uw[i]);
     }
 
     if constexpr (MODE == MODE_QUANT) {
@@ -283,8 +401,8 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
             rmax = fmaxf(rmax, bmax[i]);
         }
         float dummy1 = 0.0f, dummy2 = 0.0f;
-        row_max3<WPR>(rmax, dummy1, dummy2, red, wave, lrow);
-        const RowQ rq = row_params(rmax);
+        row_max<WPR, 1>(rmax, dummy1, dummy2, red, wave, lrow);
+        const RowQ rq = row_params_bf16(rmax);
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
             if (!valid[i]) continue;
@@ -334,11 +452,9 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
         float rmax = 0.0f;
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
-            bmax[i] = 0.0f;
-            if (!valid[i]) continue;
-            const int b = lt + T * i;
+            const int cb = c0 + T * i;
             uint32_t gw[8];
-            load_block_cached(a.gamma, 32u * (uint32_t)b, gw);
+            load_chunk(a.gamma, cb, nb, true, gw);
             float v[16], gv[16];
             unpack16(xw[i], v);
             unpack16(gw, gv);
@@ -348,13 +464,13 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
                 const float t1 = v[2 * j + 1] * r;
                 xw[i][j] = f32x2_to_bf16x2(t0 * gv[2 * j], t1 * gv[2 * j + 1]);  // y replaces x
             }
-            if (a.y) store_block(yr, 32u * (uint32_t)b, xw[i]);
-            bmax[i] = amax16_packed(xw[i]);
+            if (a.y) store_chunk(yr, cb, nb, active, xw[i]);
+            bmax[i] = valid[i] ? amax16_packed(xw[i]) : 0.0f;
             rmax = fmaxf(rmax, bmax[i]);
         }
         float dummy1 = 0.0f, dummy2 = 0.0f;
-        row_max3<WPR>(rmax, dummy1, dummy2, red, wave, lrow);
-        const RowQ rq = row_params(rmax);
+        row_max<WPR, 1>(rmax, dummy1, dummy2, red, wave, lrow);
+        const RowQ rq = row_params_bf16(rmax);
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
             if (!valid[i]) continue;
@@ -373,15 +489,13 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
         uint32_t hw[BPL][8];
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
-            hmax[i] = gmax[i] = umax[i] = 0.0f;
-            if (!valid[i]) continue;
             float sv[16];
             silu32_x16(xw[i], sig, sv);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 hw[i][j] = f32x2_to_bf16x2(sv[2 * j] * bf16_lo(uw[i][j]), sv[2 * j + 1] * bf16_hi(uw[i][j]));
-            const int b = lt + T * i;
-            if (a.y) store_block(yr, 32u * (uint32_t)b, hw[i]);
+            if (a.y) store_chunk(yr, c0 + T * i, nb, active, hw[i]);
+            // masked blocks load as zeros: their maxima are 0
             hmax[i] = amax16_packed(hw[i]);
             gmax[i] = amax16_packed(xw[i]);
             umax[i] = amax16_packed(uw[i]);
@@ -389,8 +503,8 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a) {
             rg = fmaxf(rg, gmax[i]);
             ru = fmaxf(ru, umax[i]);
         }
-        row_max3<WPR>(rh, rg, ru, red, wave, lrow);
-        const RowQ qh = row_params(rh), qg = row_params(rg), qu = row_params(ru);
+        row_max<WPR, 3>(rh, rg, ru, red, wave, lrow);
+        const RowQ qh = row_params_bf16(rh), qg = row_params_bf16(rg), qu = row_params_bf16(ru);
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
             if (!valid[i]) continue;
@@ -505,22 +619,24 @@ __device__ __forceinline__ void pack16(const float v[16], uint32_t w[8]) {
 }
 
 template <int WPR, int BPL, int MODE>
-__global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a_arg) {
+    const BwdArgs &a = kernel_args<BwdArgs>();
+    (void)a_arg;
     constexpr int NT = row_threads<WPR>();
     constexpr int T = 64 * WPR;
     constexpr int RPW = NT / T;
-    __shared__ float red[NT / 64][4];
+    __shared__ uint32_t red[NT / 64][2];
     __shared__ double redd[NT / 64][2];
-    __shared__ uint32_t tabs[MODE == MODE_SILU_BWD ? 2 * kSigTab : 1];
+    __shared__ u32x2 tabs[MODE == MODE_SILU_BWD ? kSigTabZ : 1];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lrow = tid / T;
     const int lt = tid % T;
+    const int c0 = lt & ~63;  // this wavefront's first chunk in the row (lane l: block c0 + l)
     const int cols = a.cols;
     const int nb = cols >> 4;
     if constexpr (MODE == MODE_SILU_BWD) {
-        load_sigmoid_table(tabs, tid, NT);
-        load_dsilu_table(tabs + kSigTab, tid, NT);
+        load_silu_dsilu_table_z(tabs, tid, NT);
         lds_sync();
     }
     const int64_t ngroups = (a.rows + RPW - 1) / RPW;
@@ -537,11 +653,12 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
         const bool pact = prow < a.rows;
 #pragma unroll
         for (int i = 0; i < BS; ++i) {
-            const int b = lt + T * i;
-            if (pact && b < nb) {
-                load_block(a.dy + prow * a.lddy, 32u * (uint32_t)b, pdw[i]);
-                load_codes(a.in0, prow, cols, b, pc0[i][0], pc0[i][1], ps0[i]);
-                load_codes(a.in1, prow, cols, b, pc1[i][0], pc1[i][1], ps1[i]);
+            const int cb = c0 + T * i;
+            load_chunk(a.dy + prow * a.lddy, cb, nb, pact, pdw[i]);
+            pc0[i][0] = pc0[i][1] = ps0[i] = pc1[i][0] = pc1[i][1] = ps1[i] = 0u;
+            if (pact && lt + T * i < nb) {
+                load_codes(a.in0, prow, cols, lt + T * i, pc0[i][0], pc0[i][1], ps0[i]);
+                load_codes(a.in1, prow, cols, lt + T * i, pc1[i][0], pc1[i][1], ps1[i]);
             }
         }
         pd0 = pact ? a.in0.d[prow] : 0.0f;
@@ -555,8 +672,8 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
         const bool active = row < a.rows;
         const uint16_t *dyr = a.dy + row * a.lddy;
         uint32_t dw[BPL][8];
-        uint32_t c0[BPL][2], s0[BPL];
-        uint32_t c1[MODE == MODE_SILU_BWD ? BPL : 1][2], s1[MODE == MODE_SILU_BWD ? BPL : 1];
+        uint32_t k0[BPL][2], t0[BPL];
+        uint32_t k1[MODE == MODE_SILU_BWD ? BPL : 1][2], t1[MODE == MODE_SILU_BWD ? BPL : 1];
         uint32_t cw[MODE == MODE_RMS_BWD ? BPL : 1][8];
         bool valid[BPL];
         float d0, d1 = 0.0f;
@@ -566,12 +683,12 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
                 valid[i] = active && lt + T * i < nb;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) dw[i][j] = pdw[i][j];
-                c0[i][0] = pc0[i][0];
-                c0[i][1] = pc0[i][1];
-                s0[i] = ps0[i];
-                c1[i][0] = pc1[i][0];
-                c1[i][1] = pc1[i][1];
-                s1[i] = ps1[i];
+                k0[i][0] = pc0[i][0];
+                k0[i][1] = pc0[i][1];
+                t0[i] = ps0[i];
+                k1[i][0] = pc1[i][0];
+                k1[i][1] = pc1[i][1];
+                t1[i] = ps1[i];
             }
             d0 = pd0;
             d1 = pd1;
@@ -579,15 +696,18 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
         } else {
 #pragma unroll
             for (int i = 0; i < BPL; ++i) {
+                const int cb = c0 + T * i;
                 const int b = lt + T * i;
                 valid[i] = active && b < nb;
+                load_chunk(dyr, cb, nb, active, dw[i]);
+                if constexpr (MODE == MODE_RMS_BWD) {
+                    if (a.C) load_chunk(a.C + row * a.ldc, cb, nb, active, cw[i]);
+                }
+                k0[i][0] = k0[i][1] = t0[i] = 0u;
+                if constexpr (MODE == MODE_SILU_BWD) k1[i][0] = k1[i][1] = t1[i] = 0u;
                 if (valid[i]) {
-                    load_block(dyr, 32u * (uint32_t)b, dw[i]);
-                    load_codes(a.in0, row, cols, b, c0[i][0], c0[i][1], s0[i]);
-                    if constexpr (MODE == MODE_SILU_BWD) load_codes(a.in1, row, cols, b, c1[i][0], c1[i][1], s1[i]);
-                    if constexpr (MODE == MODE_RMS_BWD) {
-                        if (a.C) load_block(a.C + row * a.ldc, 32u * (uint32_t)b, cw[i]);
-                    }
+                    load_codes(a.in0, row, cols, b, k0[i][0], k0[i][1], t0[i]);
+                    if constexpr (MODE == MODE_SILU_BWD) load_codes(a.in1, row, cols, b, k1[i][0], k1[i][1], t1[i]);
                 }
             }
             d0 = active ? a.in0.d[row] : 0.0f;
@@ -601,36 +721,24 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
             uint32_t gw[BPL][8], uw[BPL][8];  // dg, du as packed BF16
 #pragma unroll
             for (int i = 0; i < BPL; ++i) {
-                gmax[i] = umax[i] = 0.0f;
-                if (!valid[i]) continue;
+                // masked blocks hold zero codes, scales and dh: dg = du = 0
                 float R[16];
                 uint32_t gb[8];
-                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                dequant16(k0[i][0], k0[i][1], t0[i], d0, R);
                 pack16(R, gb);  // g' as BF16
                 float U[16];
-                dequant16(c1[i][0], c1[i][1], s1[i], d1, U);
+                dequant16(k1[i][0], k1[i][1], t1[i], d1, U);
                 uint32_t ub[8];
                 pack16(U, ub);  // u' as BF16
-                // table reads for all 16 elements first, then the selection
-                uint32_t ts[16], td[16];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t lo = silu32_index(gb[j] & 0xFFFFu), hi = silu32_index(gb[j] >> 16);
-                    ts[2 * j] = tabs[lo];
-                    ts[2 * j + 1] = tabs[hi];
-                    td[2 * j] = tabs[kSigTab + lo];
-                    td[2 * j + 1] = tabs[kSigTab + hi];
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(ts[j]), "+v"(td[j]));
+                float sv[16], dv[16];
+                silu_dsilu_x16(gb, tabs, sv, dv);
                 float vg[16], vu[16];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const uint32_t g16 = h ? (gb[j] >> 16) : (gb[j] & 0xFFFFu);
-                        const float sl = silu32_select(g16, ts[2 * j + h]);
-                        const float ds = dsilu32_select(g16, td[2 * j + h]);
+                        const float sl = sv[2 * j + h];
+                        const float ds = dv[2 * j + h];
                         const float d = h ? bf16_hi(dw[i][j]) : bf16_lo(dw[i][j]);
                         const float up = h ? bf16_hi(ub[j]) : bf16_lo(ub[j]);
                         vu[2 * j + h] = d * sl;
@@ -640,17 +748,16 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
                 }
                 pack16(vg, gw[i]);
                 pack16(vu, uw[i]);
-                const int b = lt + T * i;
-                if (a.o0) store_block(a.o0 + row * a.ldo, 32u * (uint32_t)b, gw[i]);
-                if (a.o1) store_block(a.o1 + row * a.ldo, 32u * (uint32_t)b, uw[i]);
+                if (a.o0) store_chunk(a.o0 + row * a.ldo, c0 + T * i, nb, active, gw[i]);
+                if (a.o1) store_chunk(a.o1 + row * a.ldo, c0 + T * i, nb, active, uw[i]);
                 gmax[i] = amax16_packed(gw[i]);
                 umax[i] = amax16_packed(uw[i]);
                 rg = fmaxf(rg, gmax[i]);
                 ru = fmaxf(ru, umax[i]);
             }
             float dummy = 0.0f;
-            row_max3<WPR>(rg, ru, dummy, red, wave, lrow);
-            const RowQ qg = row_params(rg), qu = row_params(ru);
+            row_max<WPR, 2>(rg, ru, dummy, red, wave, lrow);
+            const RowQ qg = row_params_bf16(rg), qu = row_params_bf16(ru);
 #pragma unroll
             for (int i = 0; i < BPL; ++i) {
                 if (!valid[i]) continue;
@@ -678,7 +785,7 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
             for (int i = 0; i < BPL; ++i) {
                 if (!valid[i]) continue;
                 float R[16], v[16];
-                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                dequant16(k0[i][0], k0[i][1], t0[i], d0, R);
                 unpack16(dw[i], v);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) dd_add(s, c, (double)v[j] * (double)R[j]);
@@ -707,13 +814,12 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
             uint32_t xw[BPL][8];
 #pragma unroll
             for (int i = 0; i < BPL; ++i) {
-                xmax[i] = 0.0f;
-                if (!valid[i]) continue;
-                const int b = lt + T * i;
+                // masked blocks hold zero dy, codes, gamma and C: dx = 0
+                const int cb = c0 + T * i;
                 uint32_t gmw[8];
-                load_block_cached(a.gamma, 32u * (uint32_t)b, gmw);
+                load_chunk(a.gamma, cb, nb, true, gmw);
                 float R[16], v[16], gm[16], o[16];
-                dequant16(c0[i][0], c0[i][1], s0[i], d0, R);
+                dequant16(k0[i][0], k0[i][1], t0[i], d0, R);
                 unpack16(dw[i], v);
                 unpack16(gmw, gm);
 #pragma unroll
@@ -730,14 +836,14 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a) {
                     for (int j = 0; j < 16; ++j) o[j] = o[j] + cv[j];
                 }
                 pack16(o, xw[i]);
-                if (a.o0) store_block(a.o0 + row * a.ldo, 32u * (uint32_t)b, xw[i]);
+                if (a.o0) store_chunk(a.o0 + row * a.ldo, cb, nb, active, xw[i]);
                 xmax[i] = amax16_packed(xw[i]);
                 rx = fmaxf(rx, xmax[i]);
             }
             if (a.q0.codes) {
                 float dummy1 = 0.0f, dummy2 = 0.0f;
-                row_max3<WPR>(rx, dummy1, dummy2, red, wave, lrow);
-                const RowQ rq = row_params(rx);
+                row_max<WPR, 1>(rx, dummy1, dummy2, red, wave, lrow);
+                const RowQ rq = row_params_bf16(rx);
 #pragma unroll
                 for (int i = 0; i < BPL; ++i) {
                     if (!valid[i]) continue;
