@@ -345,6 +345,28 @@ __device__ __forceinline__ void emit_block(const NV &q, int64_t row, int cols, i
     __builtin_nontemporal_store((uint8_t)sb, sr + (uint32_t)b);
 }
 
+// Binade spread of the nonzero BF16 values of a set of packed words, for the
+// exact-accumulation fast paths: the exponent of the largest magnitude minus
+// that of the smallest nonzero one (negative for an all-zero set), or 2^20
+// when a value is subnormal, infinite or NaN (such sets take the error-free
+// accumulation).
+struct MagRange {
+    uint32_t mx = 0u, mn = 0xFFFFFFFFu;  // packed largest magnitude, smallest magnitude - 1 (zero wraps)
+};
+
+__device__ __forceinline__ void mag_range_add(MagRange &r, uint32_t w) {
+    const uint32_t mag = w & 0x7FFF7FFFu;
+    r.mx = pk_max_u16(r.mx, mag);
+    r.mn = pk_min_u16(r.mn, pk_sub_u16(mag, 0x00010001u));
+}
+
+__device__ __forceinline__ int mag_spread(const MagRange &r) {
+    const uint32_t hi = max(r.mx & 0xFFFFu, r.mx >> 16);
+    const uint32_t lo = min(r.mn & 0xFFFFu, r.mn >> 16);  // 0xFFFF: no nonzero value
+    if (hi >= 0x7F80u || lo < 0x7Fu) return 1 << 20;
+    return (int)(hi >> 7) - (int)((lo + 1u) >> 7);
+}
+
 // Threads of a row kernel's workgroup: 256, or one row of 64 * WPR.
 template <int WPR>
 constexpr int row_threads() { return WPR > 4 ? 64 * WPR : 256; }
@@ -413,19 +435,41 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a_arg) 
         }
         if (active && lt == 0) a.q0.d[row] = rq.d;
     } else if constexpr (MODE == MODE_RMS) {
-        // sum of squares: squares are exact in binary64; accumulate error-free
+        // Sum of squares, exact to the last place of the double-double
+        // result.  Squares of BF16 values are exact in binary64 (16 bits).
+        // When a lane's nonzero values span at most 15 binades, each of its
+        // partial sums (at most 64 squares, masked blocks are zeros) is a
+        // multiple of the smallest square's last place and below 2^53 of them
+        // (2 * 15 + 14 + 2 + 6 <= 53), so plain binary64 accumulation is
+        // exact; otherwise the lane accumulates error-free (double-double).
         double s = 0.0, c = 0.0;
+        MagRange mr;
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            if (!valid[i]) continue;
-            float v[16];
-            unpack16(xw[i], v);
+        for (int i = 0; i < BPL; ++i)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const double xv = (double)v[j];
-                dd_add(s, c, xv * xv);
+            for (int j = 0; j < 8; ++j) mag_range_add(mr, xw[i][j]);
+        if (mag_spread(mr) <= 15) {
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                float v[16];
+                unpack16(xw[i], v);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s = __builtin_fma((double)v[j], (double)v[j], s);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                float v[16];
+                unpack16(xw[i], v);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const double xv = (double)v[j];
+                    dd_add(s, c, xv * xv);
+                }
             }
         }
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) opaque8(xw[i]);  // unpacked again below
         wave_sum_dd(s, c);
         s = __shfl(s, 0, 64);  // every lane takes lane 0's (identical) result
         c = __shfl(c, 0, 64);
@@ -875,7 +919,8 @@ static pact_status launch_bwd(const BwdArgs &a, hipStream_t st) {
     const int threads = wpr > 4 ? 64 * wpr : 256;
     const int rpw = threads / (64 * wpr);
     const int64_t groups = (a.rows + rpw - 1) / rpw;
-    // SiLU backward: the two 32 KB tables allow two resident workgroups per CU
+    // SiLU backward: the 64 KB table allows two resident workgroups per CU,
+    // which loop over row groups; RMSNorm backward: one workgroup per row group
     const int64_t cap = MODE == MODE_SILU_BWD ? (int64_t)device_cus() * 2 : groups;
     const dim3 grid((unsigned)(groups < cap ? groups : cap));
 #define PACT_BWD_CASE(W, B)                                                                   \

@@ -76,6 +76,42 @@ def test_rmsnorm_bwd_parity(rows, cols, with_c):
     G.assert_nvfp4_equal(gdxq3, dxq, "dxq (no BF16 output)")
 
 
+@pytest.mark.parametrize("cols", [3072, 9232])
+def test_rmsnorm_bwd_edge_values(cols):
+    """Edge values for the exact sum S = sum dy y' and x^ = y' / gamma: dy
+    spanning up to 120 binades, subnormal dy, a lone outlier, zero and negative
+    zero rows, sparse zeros; gamma with exact zeros (x^ = 0 there) and negative
+    entries; with and without the residual; one wavefront per row (3072) and
+    eight (9232), bit-exact against the oracle."""
+    rng = np.random.default_rng(cols + 3)
+    rows = 12
+    x = synth.to_bf16_bits(rng.standard_t(4, (rows, cols)) * 0.5)
+    g = 1.0 + 0.1 * rng.standard_normal(cols)
+    g[rng.integers(0, cols, 40)] = 0.0
+    g[rng.integers(0, cols, 40)] *= -1.0
+    gamma = synth.to_bf16_bits(g)
+    _, yq, rstd = oracle.rmsnorm_quant(x, gamma, 1e-5)
+    d = rng.standard_normal((rows, cols))
+    d[0] *= np.exp2(rng.integers(-60, 60, cols))        # wide exponent spread in every block
+    d[1] *= 1e-39                                       # subnormal BF16 values
+    d[2] = 0.0
+    d[3] = -0.0
+    d[4] *= 1e-3
+    d[4, rng.integers(cols)] = 3e4                      # one outlier
+    d[5, ::3] = 0.0                                     # sparse zeros
+    d[6] *= np.exp2(rng.integers(-12, 13, cols))        # spread near the fast path's bound
+    dy = synth.to_bf16_bits(d)
+    C = synth.to_bf16_bits(rng.standard_normal((rows, cols)))
+    for Cin in (None, C):
+        dx, dxq = oracle.rmsnorm_bwd(dy, yq, gamma, rstd, Cin)
+        gdx, gdxq = pb.pact_rmsnorm_bwd_nvfp4(G.dev_bf16(dy), G.dev_nvfp4(yq), G.dev_bf16(gamma),
+                                              torch.from_numpy(rstd).cuda(),
+                                              C=G.dev_bf16(Cin) if Cin is not None else None)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.host_bits(gdx), dx)
+        G.assert_nvfp4_equal(gdxq, dxq, "dxq")
+
+
 @pytest.mark.parametrize("shape", ["llama1b_layer", "llama3b_layer"])
 def test_backward_layer_sizes_sampled_rows(shape):
     """At the layer workloads' full sizes ([M, I] for SiLU, [M, H] for RMSNorm)
