@@ -48,6 +48,7 @@ import argparse
 import glob
 import hashlib
 import json
+import re
 import os
 import sqlite3
 import sys
@@ -66,7 +67,8 @@ GEMM_SOURCE = os.path.join(ROOT, "nvfp4_gemm_amd", "csrc", "pact_gemm.hip")
 CONFIGS = ["single_linear", "llama1b_layer", "qwen1.5b_layer", "llama3b_layer", "llama3b_stack28"]
 # kernels of the GEMM entry points: LoRA-down, one main kernel, and (split K)
 # the epilogue kernel; the main kernel's name marks one entry-point call
-GEMM_KERNELS = ("gemm_kernel", "gemm8_kernel", "lora_down_kernel", "lora_down_pipe_kernel", "splitk_epi_kernel")
+GEMM_KERNELS = ("gemm_kernel", "gemm8_kernel", "lora_down_kernel", "lora_down_pipe_kernel", "splitk_epi_kernel",
+                "lora_transpose_kernel")
 GEMM_MAIN_KERNELS = ("gemm_kernel", "gemm8_kernel")
 
 
@@ -552,12 +554,28 @@ def summarize_pmc(args):
     fdir, wdir, cfdir, cwdir = args.summarize_pmc
 
     def gemm_totals(d, counter):
-        tot, disp = 0.0, {}
+        """Traffic of the GEMM entry points' kernels and the number of entry
+        points: main-kernel dispatches, less the second launches of
+        column-split plans (a main kernel without K split whose preceding
+        dispatch is a main kernel; every other entry point starts with its
+        LoRA-down or, when that is fused, with a K-split main kernel)."""
+        tot, names = 0.0, {}
         for name, did, v in _pmc_rows(d, counter):
+            names[did] = name
             if any(m in name for m in GEMM_KERNELS):
                 tot += v
-                disp[did] = name
-        return tot, sum(1 for n in disp.values() if any(m in n for m in GEMM_MAIN_KERNELS))
+        is_main = lambda n: any(m in n for m in GEMM_MAIN_KERNELS)
+        second = re.compile(r"gemm_kernel<\d+, \d+, \d+, (true|false), false>")
+        order = sorted(names)
+        entries = 0
+        for i, did in enumerate(order):
+            n = names[did]
+            if not is_main(n):
+                continue
+            if i > 0 and second.search(n) and is_main(names[order[i - 1]]):
+                continue
+            entries += 1
+        return tot, entries
 
     def copy_kib(d, counter):
         vals = {}
@@ -623,23 +641,32 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
     calls = work.calls()
     torch.cuda.reset_peak_memory_stats()
+    cpu_s = 0.0
     for _ in range(args.warmup):
+        t0 = time.perf_counter()
         for c in calls:
             c[3]()
-    torch.cuda.synchronize()
-    # timed region: events around every call, on the stream the kernels run on
+        cpu_s = max(cpu_s, time.perf_counter() - t0)
+        torch.cuda.synchronize()
+    # timed region: events around every call, on the stream the kernels run
+    # on.  Each step starts behind a bounded GPU spin about twice as long as
+    # the host takes to issue the step, so that the step's calls are queued
+    # before the GPU reaches them and each event pair times device work only
+    # (without it the small layers' per-call times would include the host's
+    # launch latency).  The eager step time runs from the end of the spin.
+    spin_cycles = int(min(max(2.0 * cpu_s, 1e-3), 0.2) * 2.4e9)
     evs = [[(ev(), ev()) for _ in calls] for _ in range(args.steps)]
-    t_start, t_end = ev(), ev()
+    t_begin = [ev() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start.record(st)
     for s in range(args.steps):
+        torch.cuda._sleep(spin_cycles)
+        t_begin[s].record(st)
         for (a, b), c in zip(evs[s], calls):
             a.record(st)
             c[3]()
             b.record(st)
-    t_end.record(st)
     torch.cuda.synchronize()
-    eager_ms_step = t_start.elapsed_time(t_end) / args.steps
+    eager_ms_step = sum(t_begin[s].elapsed_time(evs[s][-1][1]) for s in range(args.steps)) / args.steps
     ms_step = eager_ms_step
     timing = "eager"
     if not args.eager:
