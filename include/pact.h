@@ -372,6 +372,16 @@ pact_status pact_debug_lora_down_plan(int64_t M, int64_t N, int64_t K, int32_t r
                                       int32_t *route, int32_t *npass, int32_t *rg, int32_t *rows_per_wave,
                                       int32_t *waves);
 
+/* Diagnostic: the launch shape of a row kernel for rows of `cols` elements
+ * (host only, no GPU work).  op: 0 pact_quantize_nvfp4, 1
+ * pact_rmsnorm_quant_nvfp4, 2 pact_silu_mul_quant_nvfp4, 3
+ * pact_silu_mul_bwd_quant_nvfp4, 4 pact_rmsnorm_bwd_nvfp4.  Writes the
+ * wavefronts that share one row and the 16-element blocks each lane holds.
+ * PACT_ERR_INVALID_ARG for an unknown op, cols <= 0 or a null output;
+ * PACT_ERR_UNSUPPORTED_SHAPE for cols not a multiple of 16 or above
+ * PACT_MAX_ROW (as the entry points themselves). */
+pact_status pact_debug_row_plan(int32_t op, int64_t cols, int32_t *waves_per_row, int32_t *blocks_per_lane);
+
 #ifdef __cplusplus
 }
 #endif

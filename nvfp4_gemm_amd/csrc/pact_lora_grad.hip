@@ -266,10 +266,14 @@ static size_t lora_grads_ws(int64_t M, int64_t N, int64_t K, int r) {
 template <bool NV>
 static void launch_grad_kernel(const GradArgs &g, const GradPlan &p, int jt, hipStream_t st) {
     const dim3 grid((unsigned)(g.cblocks * p.msplit + g.side.wgs));
-    if (p.cb == 256) {
-        if (jt == 1) hipLaunchKernelGGL((lora_grad_kernel<256, 1, NV>), grid, dim3(256), 0, st, g);
-        else hipLaunchKernelGGL((lora_grad_kernel<256, 2, NV>), grid, dim3(256), 0, st, g);
-    } else {
+    if constexpr (!NV) {  // 256-column blocks only for BF16 operands (grad_plan)
+        if (p.cb == 256) {
+            if (jt == 1) hipLaunchKernelGGL((lora_grad_kernel<256, 1, NV>), grid, dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((lora_grad_kernel<256, 2, NV>), grid, dim3(256), 0, st, g);
+            return;
+        }
+    }
+    {
         if (jt == 1) hipLaunchKernelGGL((lora_grad_kernel<128, 1, NV>), grid, dim3(256), 0, st, g);
         else hipLaunchKernelGGL((lora_grad_kernel<128, 2, NV>), grid, dim3(256), 0, st, g);
     }

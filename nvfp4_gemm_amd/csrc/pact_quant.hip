@@ -578,20 +578,37 @@ __global__ __launch_bounds__(row_threads<WPR>()) void row_kernel(RowArgs a_arg) 
     }  // row groups
 }
 
-template <int MODE>
-static pact_status launch_rows(const RowArgs &a, hipStream_t st) {
-    if (a.rows == 0 || a.cols == 0) return PACT_OK;
-    const int nb = a.cols / 16;
-    int wpr, bpl;
+// Wavefronts per row and 16-element blocks per lane of the row kernels for a
+// row of nb blocks (the forward kernels and, separately, the backward ones).
+static void row_shape(int mode, int64_t nb, int &wpr, int &bpl) {
+    if (mode == MODE_SILU_BWD || mode == MODE_RMS_BWD) {
+        if (nb <= 64) wpr = 1, bpl = 1;
+        else if (nb <= 128) wpr = 1, bpl = 2;
+        else if (nb <= 192) wpr = 1, bpl = 3;
+        else if (nb <= 256) wpr = 4, bpl = 1;
+        else if (nb <= 512) wpr = 8, bpl = 1;
+        else if (nb <= 1024) wpr = 8, bpl = 2;
+        else if (nb <= 1536) wpr = 8, bpl = 3;
+        else wpr = 8, bpl = 4;
+        return;
+    }
     if (nb <= 64) wpr = 1, bpl = 1;
     else if (nb <= 128) wpr = 1, bpl = 2;
     else if (nb <= 192) wpr = 1, bpl = 3;
     else if (nb <= 256) wpr = 4, bpl = 1;
     else if (nb <= 512) wpr = 4, bpl = 2;
-    else if (nb <= 768 && MODE != MODE_SILU) wpr = 4, bpl = 3;
+    else if (nb <= 768 && mode != MODE_SILU) wpr = 4, bpl = 3;
     else if (nb <= 1024) wpr = 8, bpl = 2;
     else if (nb <= 1536) wpr = 8, bpl = 3;
     else wpr = 8, bpl = 4;
+}
+
+template <int MODE>
+static pact_status launch_rows(const RowArgs &a, hipStream_t st) {
+    if (a.rows == 0 || a.cols == 0) return PACT_OK;
+    const int nb = a.cols / 16;
+    int wpr, bpl;
+    row_shape(MODE, nb, wpr, bpl);
     const int threads = wpr > 4 ? 64 * wpr : 256;
     const int rpw = threads / (64 * wpr);
     const int64_t groups = (a.rows + rpw - 1) / rpw;
@@ -609,8 +626,7 @@ static pact_status launch_rows(const RowArgs &a, hipStream_t st) {
     PACT_ROWS_CASE(1, 3)
     PACT_ROWS_CASE(4, 1)
     PACT_ROWS_CASE(4, 2)
-    PACT_ROWS_CASE(4, 3)
-    PACT_ROWS_CASE(8, 1)
+    if constexpr (MODE != MODE_SILU) PACT_ROWS_CASE(4, 3)
     PACT_ROWS_CASE(8, 2)
     PACT_ROWS_CASE(8, 3)
     PACT_ROWS_CASE(8, 4)
@@ -908,14 +924,7 @@ static pact_status launch_bwd(const BwdArgs &a, hipStream_t st) {
     if (a.rows == 0 || a.cols == 0) return PACT_OK;
     const int nb = a.cols / 16;
     int wpr, bpl;
-    if (nb <= 64) wpr = 1, bpl = 1;
-    else if (nb <= 128) wpr = 1, bpl = 2;
-    else if (nb <= 192) wpr = 1, bpl = 3;
-    else if (nb <= 256) wpr = 4, bpl = 1;
-    else if (nb <= 512) wpr = 8, bpl = 1;
-    else if (nb <= 1024) wpr = 8, bpl = 2;
-    else if (nb <= 1536) wpr = 8, bpl = 3;
-    else wpr = 8, bpl = 4;
+    row_shape(MODE, nb, wpr, bpl);
     const int threads = wpr > 4 ? 64 * wpr : 256;
     const int rpw = threads / (64 * wpr);
     const int64_t groups = (a.rows + rpw - 1) / rpw;
@@ -1128,4 +1137,16 @@ extern "C" pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t
     const unsigned blocks = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(dsilu_probe_kernel, dim3(blocks), dim3(256), 0, as_stream(stream), g, out, n);
     return launch_status();
+}
+
+extern "C" pact_status pact_debug_row_plan(int32_t op, int64_t cols, int32_t *waves_per_row,
+                                           int32_t *blocks_per_lane) {
+    if (op < 0 || op > 4 || cols <= 0 || !waves_per_row || !blocks_per_lane) return PACT_ERR_INVALID_ARG;
+    PACT_TRY(check_row_len(0, cols));
+    static const int kModes[5] = {MODE_QUANT, MODE_RMS, MODE_SILU, MODE_SILU_BWD, MODE_RMS_BWD};
+    int wpr, bpl;
+    row_shape(kModes[op], cols / 16, wpr, bpl);
+    *waves_per_row = wpr;
+    *blocks_per_lane = bpl;
+    return PACT_OK;
 }

@@ -42,7 +42,8 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_rmsnorm_bwd_nvfp4", "pact_debug_dsilu32", "pact_lora_grads_workspace",
            "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
            "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc",
-           "pact_debug_gemm_plan_columns", "pact_gptq_hessian_nvfp4", "pact_gptq_workspace", "pact_gptq_nvfp4"]
+           "pact_debug_gemm_plan_columns", "pact_gptq_hessian_nvfp4", "pact_gptq_workspace", "pact_gptq_nvfp4",
+           "pact_debug_row_plan"]
 
 
 class PactError(RuntimeError):
@@ -116,6 +117,8 @@ def lib():
         I32P = ctypes.POINTER(ctypes.c_int32)
         L.pact_debug_gemm_plan_columns.restype = st
         L.pact_debug_gemm_plan_columns.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
+        L.pact_debug_row_plan.restype = st
+        L.pact_debug_row_plan.argtypes = [ctypes.c_int32, I64, I32P, I32P]
         L.pact_debug_lora_down_plan.restype = st
         L.pact_debug_lora_down_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 I32P, I32P, I32P, I32P, I32P]
@@ -494,6 +497,17 @@ def pact_debug_gemm_plan_columns(M: int, N: int, K: int, r: int = 0, dgrad: bool
     _check(lib().pact_debug_gemm_plan_columns(M, N, K, r, 1 if dgrad else 0, ctypes.byref(n1), ctypes.byref(k2)),
            "pact_debug_gemm_plan_columns")
     return n1.value, k2.value
+
+
+ROW_OPS = {"quantize": 0, "rmsnorm_quant": 1, "silu_mul_quant": 2, "silu_mul_bwd": 3, "rmsnorm_bwd": 4}
+
+
+def pact_debug_row_plan(op: str, cols: int) -> tuple[int, int]:
+    """(wavefronts per row, 16-element blocks per lane) of the row kernel of
+    op (a ROW_OPS key) for rows of cols elements."""
+    w, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pact_debug_row_plan(ROW_OPS[op], cols, ctypes.byref(w), ctypes.byref(b)), "pact_debug_row_plan")
+    return w.value, b.value
 
 
 LORA_DOWN_ROUTES = {1: "fused into the split-K launch", 2: "pipelined", 3: "transpose, then pipelined",

@@ -300,3 +300,30 @@ def test_adamw_validation(L):
     assert f(FAKE, None, FAKE, FAKE, FAKE, 16, *hp, 1, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE + 4, FAKE, 16, *hp, 1, None) == 3
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 8, 16, *hp, 1, None) == 3
+
+
+def test_row_plan_host_logic(L):
+    """The row kernels' launch shapes: the nine widths of the GPU variant test
+    select every compiled (wavefronts per row, blocks per lane) of each row
+    kernel, a shape covers the row (64 lanes x wavefronts x blocks >= blocks of
+    the row), and invalid arguments are rejected like the entry points do."""
+    from tests.test_gpu_variant_coverage import WIDTHS
+    i32 = ctypes.c_int32
+    w, b = i32(), i32()
+    fwd = {(1, 1), (1, 2), (1, 3), (4, 1), (4, 2), (4, 3), (8, 2), (8, 3), (8, 4)}
+    bwd = {(1, 1), (1, 2), (1, 3), (4, 1), (8, 1), (8, 2), (8, 3), (8, 4)}
+    compiled = {0: fwd, 1: fwd, 2: fwd - {(4, 3)}, 3: bwd, 4: bwd}
+    for op, shapes in compiled.items():
+        seen = set()
+        for cols in WIDTHS + [16, 48, 4096, 8960, 9232, 32768]:
+            assert L.pact_debug_row_plan(op, cols, ctypes.byref(w), ctypes.byref(b)) == 0
+            assert (w.value, b.value) in shapes
+            assert 64 * w.value * b.value >= cols // 16
+            if cols in WIDTHS:
+                seen.add((w.value, b.value))
+        assert seen == shapes, (op, shapes - seen)
+    assert L.pact_debug_row_plan(5, 1024, ctypes.byref(w), ctypes.byref(b)) == 1
+    assert L.pact_debug_row_plan(0, 0, ctypes.byref(w), ctypes.byref(b)) == 1
+    assert L.pact_debug_row_plan(0, 1024, None, ctypes.byref(b)) == 1
+    assert L.pact_debug_row_plan(0, 40, ctypes.byref(w), ctypes.byref(b)) == 2
+    assert L.pact_debug_row_plan(0, 32784, ctypes.byref(w), ctypes.byref(b)) == 2
