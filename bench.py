@@ -41,6 +41,11 @@ Other modes (used to calibrate and summarize rocprofv3 counter runs):
   --copy-calibration MIB   runs a plain device-to-device copy of MIB MiB
   --summarize-pmc DIR ...  turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                            databases into the HBM-traffic summary text
+  --library-gemm           times the vendor library's FP16 GEMM (hipBLASLt
+                           through torch) on FP16 operands of the shapes of
+                           one layer's frozen GEMMs, beside libpact's NVFP4
+                           entry points on the same shapes: a practical
+                           ceiling for the MFMA fraction
 """
 from __future__ import annotations
 
@@ -99,6 +104,7 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--pmc-out", default="")
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--library-gemm", action="store_true")
     return ap.parse_args()
 
 
@@ -502,6 +508,70 @@ def isolated_timing(torch, calls, reps=10):
     return out
 
 
+def library_gemm(args):
+    """One layer's frozen GEMMs (forward and input gradient, grouped as in the
+    step) timed two ways on the same GPU: libpact's NVFP4 entry points (frozen
+    GEMM plus the fused rank-r LoRA, from packed codes and scales) and the
+    vendor library's FP16 GEMM on FP16 operands of the same shape (torch's
+    F.linear with the weight as N x K rows, and a @ b with b as K x N; the
+    faster of the two counts).  Both rates are frozen FLOPs 2 M N K over the
+    mean time of 20 back-to-back calls."""
+    import torch
+    import torch.nn.functional as F
+    from nvfp4_gemm_amd import synth
+    if args.config == "single_linear":
+        sys.exit("--library-gemm takes a layer configuration")
+    shape = synth.LAYERS[args.config]
+    M, H, I, KV = shape.tokens, shape.hidden, shape.inter, shape.kv
+    # (entry point, N, K) in the order of the step's GEMM calls
+    gemms = [("fwd qkv", H + 2 * KV, H), ("fwd o", H, H), ("fwd gate|up", 2 * I, H), ("fwd down", H, I),
+             ("dgrad down", I, H), ("dgrad gate", H, I), ("dgrad up", H, I), ("dgrad o", H, H),
+             ("dgrad q", H, H), ("dgrad k", H, KV), ("dgrad v", H, KV)]
+    work = Stack(shape, args.seed, 1)
+    ours = [c for c in work.calls() if c[0] in ("gemm_fwd", "gemm_dgrad")]
+    assert len(ours) == len(gemms), len(ours)
+    for c, (nm, n, k) in zip(ours, gemms):
+        assert c[1] == 2 * M * n * k, (nm, c[1])
+    for c in work.calls():      # the step once, so every input of the GEMM calls is set
+        c[3]()
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # us
+
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    print(f"workload {work.config()['workload']}: one layer's frozen GEMMs, M = {M}")
+    print(f"{'entry point':<12} {'N':>6} {'K':>6}  {'NVFP4 us':>9} {'TFLOP/s':>8}  {'lib FP16 us':>11} {'TFLOP/s':>8}"
+          f"  {'ratio':>5}")
+    tot = [0.0, 0.0, 0]
+    for c, (nm, n, k) in zip(ours, gemms):
+        us_ours = timed(c[3])
+        x = torch.randn(M, k, dtype=torch.float16, device="cuda", generator=g)
+        w = torch.randn(n, k, dtype=torch.float16, device="cuda", generator=g)
+        wt = w.t().contiguous()
+        us_lib = min(timed(lambda: F.linear(x, w)), timed(lambda: x @ wt))
+        del x, w, wt
+        fl = 2 * M * n * k
+        tot[0] += us_ours
+        tot[1] += us_lib
+        tot[2] += fl
+        print(f"{nm:<12} {n:>6} {k:>6}  {us_ours:>9.1f} {fl / us_ours / 1e6:>8.1f}  {us_lib:>11.1f} "
+              f"{fl / us_lib / 1e6:>8.1f}  {us_lib / us_ours:>5.2f}", flush=True)
+    r_ours, r_lib = tot[2] / tot[0] / 1e6, tot[2] / tot[1] / 1e6
+    print(f"{'layer total':<26} {tot[0]:>9.1f} {r_ours:>8.1f}  {tot[1]:>11.1f} {r_lib:>8.1f}  {tot[1] / tot[0]:>5.2f}")
+    print(f"fraction of the {PEAK_F16_MFMA_TFLOPS:.0f} TFLOP/s dense FP16 MFMA peak: NVFP4 entry points "
+          f"{r_ours / PEAK_F16_MFMA_TFLOPS:.3f}, library FP16 GEMM {r_lib / PEAK_F16_MFMA_TFLOPS:.3f}")
+
+
 def gemm_source_sha():
     with open(GEMM_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -630,6 +700,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.library_gemm:
+        library_gemm(args)
+        return
     import torch
     from nvfp4_gemm_amd import synth
     if args.config == "single_linear":
@@ -720,9 +793,12 @@ def main():
         elif k["lora_flops"]:
             d["lora_tflops"] = k["lora_flops"] / (k["ms"] * 1e-3) / 1e12
         if k["bytes"]:
+            # algorithmic bytes over in-step time: inputs written just before
+            # can still be in the Infinity Cache, so this is not HBM bandwidth
+            # (the cache-flushed figures are under kernels_isolated_cache_flushed)
             gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
-            d["GB/s"] = gbs
-            d["hbm_frac"] = gbs / PEAK_HBM_GBS
+            d["alg_GB/s"] = gbs
+            d["alg_frac_of_hbm_peak"] = gbs / PEAK_HBM_GBS
         kinds[kind] = d
     cfg = work.config()
     out = {
