@@ -480,11 +480,15 @@ def cpu_baseline_linear(lin):
 
 
 def isolated_timing(torch, calls, reps=10):
-    """Cache-flushed timing of the memory-bound kernels: for the largest call
-    of each kind, each repetition first overwrites a 512 MiB buffer (larger
-    than the 256 MB Infinity Cache) with a fill kernel, then times the call
-    alone with events on its stream.  Reports the median."""
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    """Cold-cache timing of the memory-bound kernels: for the largest call of
+    each kind, each repetition first reads a 512 MiB buffer (twice the 256 MB
+    Infinity Cache) with a reduction kernel, then times the call alone with
+    events on its stream.  Reports the median.  The read pass evicts what the
+    caches held, writing back what was dirty, before the timed region, so the
+    call starts with its inputs in HBM only and with nothing of its own to
+    write back.  (Overwriting the buffer instead would leave the cache full of
+    dirty lines whose write-back the timed call would pay for.)"""
+    flush = torch.zeros((512 << 20) // 4, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     out = {}
     for kind in ("rmsnorm_quant", "quantize", "silu_mul_quant", "silu_mul_bwd", "rmsnorm_bwd", "adamw"):
@@ -494,7 +498,7 @@ def isolated_timing(torch, calls, reps=10):
         c = max(cs, key=lambda c: c[2])
         ts = []
         for _ in range(reps + 1):
-            flush.zero_()
+            flush.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(st)
             c[3]()
