@@ -105,6 +105,10 @@ def parse():
     ap.add_argument("--pmc-out", default="")
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--library-gemm", action="store_true")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="stream each row kernel's read and write bytes with the streaming diagnostic and "
+                         "compare the kernel's cold-cache rate with that ceiling (plus read-only, write-only "
+                         "and copy at 1 GiB)")
     return ap.parse_args()
 
 
@@ -512,6 +516,56 @@ def isolated_timing(torch, calls, reps=10):
     return out
 
 
+# Algorithmic (read, write) bytes per element of each row kernel's largest
+# call (per-row scalars left out): the inputs it must read and the outputs it
+# must write, as in the kernels' roofline table.
+ROW_MIX = {"quantize": (2.0, 0.5625), "rmsnorm_quant": (2.0, 2.5625), "silu_mul_quant": (4.0, 3.6875),
+           "silu_mul_bwd": (3.125, 5.125), "rmsnorm_bwd": (4.5625, 2.5625), "adamw": (16.0, 14.0)}
+
+
+def hbm_ceiling(torch, calls, reps=10):
+    """The HBM ceiling of each row kernel's read/write mix.  For the largest
+    call of each kind, pact_debug_stream moves the same total bytes split in
+    the kernel's read:write ratio, with the same cold-cache protocol as
+    isolated_timing (a 512 MiB read pass before every timed repetition); the
+    kernel's own cold-cache rate is then given as a fraction of that
+    ceiling.  Plain read-only, write-only and copy streams of 1 GiB are
+    reported beside them."""
+    from nvfp4_gemm_amd import pact as pb
+    kern = isolated_timing(torch, calls, reps)
+    flush = torch.zeros((512 << 20) // 4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def timed(rb, wb):
+        src = torch.arange(max(rb, 16) // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty(max(wb, 16) // 4, dtype=torch.int32, device="cuda")
+        ts = []
+        for _ in range(reps + 1):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            pb.pact_debug_stream(src if rb else None, rb, dst, wb)
+            b.record(st)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts[1:]))
+        return {"read_bytes": rb, "write_bytes": wb, "median_us": ms * 1e3,
+                "GB/s": (rb + wb) / (ms * 1e-3) / 1e9}
+
+    out = {"streams_1GiB": {"read_only": timed(1 << 30, 0), "write_only": timed(0, 1 << 30),
+                            "copy": timed(1 << 30, 1 << 30)}}
+    for kind, k in kern.items():
+        rd, wr = ROW_MIX[kind]
+        rb = int(k["bytes"] * rd / (rd + wr)) // 16 * 16
+        wb = (k["bytes"] - rb) // 16 * 16
+        s = timed(rb, wb)
+        out[kind] = {"kernel_bytes": k["bytes"], "kernel_us": k["median_us"], "kernel_GB/s": k["GB/s"],
+                     "kernel_frac_of_8TBs": k["hbm_frac"], "stream_same_mix": s,
+                     "kernel_frac_of_stream": k["GB/s"] / s["GB/s"]}
+    del flush
+    return out
+
+
 def library_gemm(args):
     """One layer's frozen GEMMs (forward and input gradient, grouped as in the
     step) timed two ways on the same GPU: libpact's NVFP4 entry points (frozen
@@ -717,6 +771,13 @@ def main():
     st = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     calls = work.calls()
+    if args.hbm_ceiling:
+        for c in calls:  # one untimed pass: every output written once
+            c[3]()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": work.config()["workload"], "hbm_ceiling": hbm_ceiling(torch, calls)}),
+              flush=True)
+        return
     torch.cuda.reset_peak_memory_stats()
     cpu_s = 0.0
     for _ in range(args.warmup):

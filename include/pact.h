@@ -333,6 +333,20 @@ pact_status pact_debug_sigmoid32(const uint16_t *g, float *out, int64_t n, void 
  * backward uses) for n BF16 inputs g.  Device pointers; stream-ordered. */
 pact_status pact_debug_dsilu32(const uint16_t *g, float *out, int64_t n, void *stream);
 
+/* Diagnostic, not part of the data flow: the HBM ceiling of a read/write mix.
+ * Reads read_bytes from src and writes write_bytes to dst with the row
+ * kernels' access pattern (consecutive lanes on consecutive 16-byte chunks,
+ * cached loads, nontemporal stores) and no other work, so its duration is
+ * what the memory system delivers for that mix and size.  Chunk c (16 bytes)
+ * of dst, c < write_bytes / 16, receives the bitwise xor of the chunks of src
+ * that the same thread read up to and including chunk c (zero when none);
+ * with write_bytes == 0, dst needs 16 bytes and is left unchanged for a
+ * zero-filled source.  Device pointers; stream-ordered.  Errors:
+ * PACT_ERR_INVALID_ARG for negative sizes, a null dst, or a null src with
+ * read_bytes > 0; PACT_ERR_MISALIGNED for sizes or pointers not multiples
+ * of 16. */
+pact_status pact_debug_stream(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes, void *stream);
+
 /* Diagnostic: the launch plan of a GEMM with output [M][N] contracted over K
  * with LoRA rank r (0: none) on the current device, as pact_gemm_nvfp4_fwd
  * (dgrad == 0) or pact_gemm_nvfp4_dgrad (dgrad != 0) chooses it given the

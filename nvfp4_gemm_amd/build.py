@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpact.so")
 SOURCES = ["pact_api.hip", "pact_quant.hip", "pact_layout.hip", "pact_gemm.hip", "pact_lora_grad.hip",
-           "pact_optim.hip", "pact_gptq.hip"]
+           "pact_optim.hip", "pact_gptq.hip", "pact_diag.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -43,7 +43,7 @@ EXPORTS = ["pact_version", "pact_status_string", "pact_quantize_nvfp4",
            "pact_lora_grads_nvfp4", "pact_adamw_step", "pact_gemm_nvfp4_fwd_grouped",
            "pact_debug_lora_down_plan", "pact_noalloc_scratch_bytes", "pact_gemm_nvfp4_fwd_noalloc",
            "pact_debug_gemm_plan_columns", "pact_gptq_hessian_nvfp4", "pact_gptq_workspace", "pact_gptq_nvfp4",
-           "pact_debug_row_plan"]
+           "pact_debug_row_plan", "pact_debug_stream"]
 
 
 class PactError(RuntimeError):
@@ -99,6 +99,8 @@ def lib():
         L.pact_adamw_step.argtypes = [P, P, P, P, P, I64, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, I64, P]
         L.pact_debug_dsilu32.restype = st
         L.pact_debug_dsilu32.argtypes = [P, P, I64, P]
+        L.pact_debug_stream.restype = st
+        L.pact_debug_stream.argtypes = [P, I64, P, I64, P]
         L.pact_debug_gemm_plan.restype = st
         L.pact_debug_gemm_plan.argtypes = [I64, I64, I64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
@@ -471,6 +473,13 @@ def pact_debug_dsilu32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:
     _check(lib().pact_debug_dsilu32(_ptr(g_bits), _ptr(out), g_bits.numel(), _stream(stream)),
            "pact_debug_dsilu32")
     return out
+
+
+def pact_debug_stream(src, read_bytes: int, dst: torch.Tensor, write_bytes: int, stream=None) -> None:
+    """Streams read_bytes of src and write_bytes of dst (the HBM-ceiling
+    diagnostic; src may be None when read_bytes is 0)."""
+    _check(lib().pact_debug_stream(_ptr(src) if src is not None else None, int(read_bytes), _ptr(dst),
+                                   int(write_bytes), _stream(stream)), "pact_debug_stream")
 
 
 def pact_debug_sigmoid32(g_bits: torch.Tensor, stream=None) -> torch.Tensor:

@@ -327,3 +327,17 @@ def test_row_plan_host_logic(L):
     assert L.pact_debug_row_plan(0, 1024, None, ctypes.byref(b)) == 1
     assert L.pact_debug_row_plan(0, 40, ctypes.byref(w), ctypes.byref(b)) == 2
     assert L.pact_debug_row_plan(0, 32784, ctypes.byref(w), ctypes.byref(b)) == 2
+
+
+def test_stream_diagnostic_validation(L):
+    """The HBM-ceiling diagnostic rejects bad arguments before any device work."""
+    f = L.pact_debug_stream
+    assert f(FAKE, -16, FAKE, 16, None) == 1
+    assert f(FAKE, 16, FAKE, -16, None) == 1
+    assert f(FAKE, 16, None, 16, None) == 1
+    assert f(None, 16, FAKE, 16, None) == 1
+    assert f(FAKE, 8, FAKE, 16, None) == 3
+    assert f(FAKE, 16, FAKE, 24, None) == 3
+    assert f(FAKE + 4, 16, FAKE, 16, None) == 3
+    assert f(FAKE, 16, FAKE + 8, 16, None) == 3
+    assert f(None, 0, FAKE, 0, None) == 0  # nothing to move: no launch
