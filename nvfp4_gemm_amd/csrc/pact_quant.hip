@@ -678,8 +678,18 @@ __device__ __forceinline__ void pack16(const float v[16], uint32_t w[8]) {
     for (int j = 0; j < 8; ++j) w[j] = f32x2_to_bf16x2(v[2 * j], v[2 * j + 1]);
 }
 
+// Occupancy floor of a backward kernel: the RMSNorm backward is held to
+// 4 wavefronts per SIMD (at most 128 VGPRs) in the shapes where the compiler
+// meets that without spilling (not 8 wavefronts per row x 3 blocks per lane,
+// nor 4 blocks per lane).
 template <int WPR, int BPL, int MODE>
-__global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a_arg) {
+constexpr int bwd_min_waves() {
+    return MODE == MODE_RMS_BWD && BPL <= 3 && !(WPR == 8 && BPL == 3) ? 4 : 1;
+}
+
+template <int WPR, int BPL, int MODE>
+__global__ __launch_bounds__(row_threads<WPR>()) __attribute__((amdgpu_waves_per_eu(bwd_min_waves<WPR, BPL, MODE>())))
+void bwd_kernel(BwdArgs a_arg) {
     const BwdArgs &a = kernel_args<BwdArgs>();
     (void)a_arg;
     constexpr int NT = row_threads<WPR>();
@@ -760,9 +770,6 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a_arg) 
                 const int b = lt + T * i;
                 valid[i] = active && b < nb;
                 load_chunk(dyr, cb, nb, active, dw[i]);
-                if constexpr (MODE == MODE_RMS_BWD) {
-                    if (a.C) load_chunk(a.C + row * a.ldc, cb, nb, active, cw[i]);
-                }
                 k0[i][0] = k0[i][1] = t0[i] = 0u;
                 if constexpr (MODE == MODE_SILU_BWD) k1[i][0] = k1[i][1] = t1[i] = 0u;
                 if (valid[i]) {
@@ -890,6 +897,9 @@ __global__ __launch_bounds__(row_threads<WPR>()) void bwd_kernel(BwdArgs a_arg) 
                     o[j] = (g - t) * r;
                 }
                 if (a.C) {
+                    // C is read only here, after the row sum, so that it does
+                    // not hold registers through the reduction
+                    load_chunk(a.C + row * a.ldc, cb, nb, active, cw[i]);
                     float cv[16];
                     unpack16(cw[i], cv);
 #pragma unroll
