@@ -101,6 +101,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB_DIR", "WRITE_DB_DIR", "COPY_FETCH_DIR",
                                                          "COPY_WRITE_DIR"))
+    ap.add_argument("--summarize-row-pmc", nargs=5, metavar=("FETCH_DB_DIR", "WRITE_DB_DIR", "COPY_FETCH_DIR",
+                                                             "COPY_WRITE_DIR", "KERNEL_STATS_CSV"),
+                    help="row-kernel HBM traffic of the 3B-shaped stack (M = 8192) from counter runs, with the "
+                         "durations of a kernel trace")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--pmc-out", default="")
     ap.add_argument("--pmc-command", default="")
@@ -743,10 +747,84 @@ def summarize_pmc(args):
     print(text, end="")
 
 
+# Row-kernel calls of the 3B-shaped layers (M = 8192, hidden 3072, intermediate
+# 8192, kv 1024): kernel instantiation -> (call, rows, cols, algorithmic bytes
+# per element, bytes per row), as in the kernels' roofline table.
+ROW_CALLS_3B = {
+    "row_kernel<1, 3, 1>": ("RMSNorm-quantize 8192x3072", 8192, 3072, 2.0 + 2.5625, 8),
+    "row_kernel<1, 3, 0>": ("quantize 8192x3072", 8192, 3072, 2.5625, 4),
+    "row_kernel<1, 1, 0>": ("quantize 8192x1024", 8192, 1024, 2.5625, 4),
+    "row_kernel<4, 2, 2>": ("SiLU-multiply-quantize 8192x8192", 8192, 8192, 4.0 + 3.6875, 12),
+    "bwd_kernel<8, 1, 3>": ("SiLU-multiply backward 8192x8192", 8192, 8192, 3.125 + 5.125, 16),
+    "bwd_kernel<1, 3, 4>": ("RMSNorm backward 8192x3072 (+ residual)", 8192, 3072, 4.5625 + 2.5625, 12),
+}
+
+
+def summarize_row_pmc(args):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of each row kernel, scaled by the
+    copy calibration, against its algorithmic bytes; durations from the
+    kernel-trace statistics of the same workload."""
+    fdir, wdir, cfdir, cwdir, stats = args.summarize_row_pmc
+
+    def copy_kib(d, counter):
+        vals = {}
+        for name, did, v in _pmc_rows(d, counter):
+            if "copy" in name.lower() or "elementwise" in name.lower():
+                vals[did] = vals.get(did, 0.0) + v
+        return max(vals.values())
+
+    def per_kernel(d, counter):
+        acc = {}
+        for name, did, v in _pmc_rows(d, counter):
+            for k in ROW_CALLS_3B:
+                if k in name:
+                    a = acc.setdefault(k, {})
+                    a[did] = a.get(did, 0.0) + v
+        return {k: (len(a), sum(a.values()) / len(a)) for k, a in acc.items()}
+
+    import csv
+    avg_us = {}
+    with open(stats) as f:
+        for r in csv.DictReader(f):
+            for k in ROW_CALLS_3B:
+                if k in r["Name"]:
+                    avg_us[k] = float(r["AverageNs"]) / 1e3
+    sf = args.copy_bytes / (copy_kib(cfdir, "FETCH_SIZE") * 1024.0)
+    sw = args.copy_bytes / (copy_kib(cwdir, "WRITE_SIZE") * 1024.0)
+    fe, wr = per_kernel(fdir, "FETCH_SIZE"), per_kernel(wdir, "WRITE_SIZE")
+    lines = ["# HBM traffic of the row kernels (fused quantizers and nonlinear backward) in the 28-layer",
+             "# llama3.2-3b-shaped stack (M=8192): rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, summed",
+             "# over the device), each scaled by the value the same counter reads for a plain device copy,",
+             "# against the algorithmic bytes (every input byte read once, every output byte written once).",
+             "# Durations: the same workload's kernel trace (eager and graph-replayed steps).  Both counters",
+             "# count traffic between L2 and the fabric, which includes Infinity-Cache (MALL) hits.",
+             f"command: {args.pmc_command}",
+             f"fetch_scale: {sf:.4f}  write_scale: {sw:.4f}", "",
+             f"{'kernel':<24} {'call':<42} {'disp':>5} {'alg MB':>8} {'read MB':>8} {'write MB':>9} "
+             f"{'cnt/alg':>8} {'avg us':>7} {'alg TB/s':>9} {'of 8':>6}"]
+    for k, (call, rows, cols, per_el, per_row) in ROW_CALLS_3B.items():
+        if k not in fe or k not in wr:
+            continue
+        alg = rows * cols * per_el + rows * per_row
+        rd, wt = fe[k][1] * 1024.0 * sf, wr[k][1] * 1024.0 * sw
+        us = avg_us.get(k, float("nan"))
+        tbs = alg / (us * 1e-6) / 1e12
+        lines.append(f"{k:<24} {call:<42} {fe[k][0]:>5} {alg / 1e6:>8.1f} {rd / 1e6:>8.1f} {wt / 1e6:>9.1f} "
+                     f"{(rd + wt) / alg:>8.2f} {us:>7.1f} {tbs:>9.2f} {tbs / 8.0:>6.3f}")
+    text = "\n".join(lines) + "\n"
+    if args.pmc_out:
+        with open(args.pmc_out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_row_pmc:
+        summarize_row_pmc(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
