@@ -105,6 +105,9 @@ def parse():
                                                              "COPY_WRITE_DIR", "KERNEL_STATS_CSV"),
                     help="row-kernel HBM traffic of the 3B-shaped stack (M = 8192) from counter runs, with the "
                          "durations of a kernel trace")
+    ap.add_argument("--summarize-coverage", metavar="KERNEL_STATS_CSV",
+                    help="kernel-variant coverage: every kernel compiled into libpact.so (from the compiler's "
+                         "resource-usage remarks) against the launches in a kernel trace of the GPU test suite")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--pmc-out", default="")
     ap.add_argument("--pmc-command", default="")
@@ -818,10 +821,58 @@ def summarize_row_pmc(args):
     print(text, end="")
 
 
+def summarize_coverage(args):
+    """Every kernel instantiation compiled into libpact.so, from hipcc's
+    resource-usage remarks on each source (compiled again for this, same
+    flags), against the number of launches of each in the kernel-trace
+    statistics of one run of the GPU test suite."""
+    import csv
+    import subprocess
+    from nvfp4_gemm_amd import build as B
+    os.makedirs(B.BUILD, exist_ok=True)
+    compiled = []
+    for src in B.SOURCES:
+        r = subprocess.run([B.HIPCC, *B.FLAGS, "-I", B.BUILD, "-c", os.path.join(B.CSRC, src), "-o", os.devnull,
+                            "-Rpass-analysis=kernel-resource-usage"], capture_output=True, text=True)
+        names = re.findall(r"Function Name: (\S+)", r.stderr)
+        if r.returncode != 0:
+            raise SystemExit(f"hipcc failed for {src}: {r.stderr[-400:]}")
+        if not names:  # a source without kernels (the version and status strings)
+            continue
+        dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+        compiled += [(src, d.strip()) for d in dem if d.strip()]
+    tidy = lambda n: n.replace("pact::", "").replace("(anonymous namespace)::", "").strip().strip('"')
+    launches = {}
+    with open(args.summarize_coverage) as f:
+        for r in csv.DictReader(f):
+            launches[tidy(r["Name"])] = launches.get(tidy(r["Name"]), 0) + int(r["Calls"])
+    lines = ["# Kernel-variant coverage of the GPU test suite: every kernel instantiation compiled into libpact.so",
+             "# (from the compiler's resource-usage remarks, per source file) and how many times the kernel trace of",
+             "# one run of the GPU test suite saw it launched.",
+             f"command: {args.pmc_command}", "", f"{'source':<20} {'launches':>9}  kernel"]
+    seen = 0
+    for src, k in compiled:
+        key = tidy(k)
+        n = launches.get(key, 0)
+        if n == 0:  # the trace prints 'void ' before templates; the demangler does not
+            n = launches.get("void " + key, 0)
+        seen += n > 0
+        lines.append(f"{src:<20} {n:>9}  {key}")
+    lines += ["", f"# {len(compiled)} compiled kernels, {seen} launched"]
+    text = "\n".join(lines) + "\n"
+    if args.pmc_out:
+        with open(args.pmc_out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_coverage:
+        summarize_coverage(args)
         return
     if args.summarize_row_pmc:
         summarize_row_pmc(args)
